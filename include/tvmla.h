@@ -1,0 +1,181 @@
+/*
+ * tvmla.h -- tree-verify attention over an MLA latent KV cache, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One call computes the verify attention of a speculative-decoding draft tree:
+ * every draft token of every request attends, with every head, to the
+ * request's prefix keys and to the draft keys its visibility mask allows.
+ * This is the call described on "The Architecture of Capture Safety:
+ * Designing a CUDA Graph-Compatible Verify Kernel for SGLang", section "The
+ * Design Emerges": a split-K flash-decode over a fixed number of splits
+ * (first insight), prefix keys through kv_indices/kv_indptr and draft keys
+ * through out_cache_loc with no concatenated copy (second insight), the raw
+ * custom_mask/mask_indptr indexed in the kernel (third insight), prefix
+ * lengths derived on the device from kv_indptr (fourth insight), and a
+ * workspace the caller allocates once (fifth insight). The cache layout is
+ * MLA's: one latent row per token, shared by every head, serving as the value
+ * and as the first 512 entries of the key ("The Plan Document", section "The
+ * Design Reasoning").
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers unless stated otherwise; the
+ *     caller owns every buffer (workspace included). The library allocates
+ *     nothing, keeps no global mutable state, and never synchronises; each
+ *     call only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream). It is safe to capture into a hipGraph: the launch
+ *     configuration depends only on the scalar arguments, so prefix lengths,
+ *     tree shapes and masks may change between replays at fixed addresses.
+ *   - Argument checks run on the host before anything is enqueued. On error
+ *     the call returns a status != TVMLA_OK and enqueues nothing. Index
+ *     CONTENTS (slots, offsets, mask bytes) are trusted: a slot outside the
+ *     cache or an offset outside its array is undefined behaviour.
+ *   - Per request b: P_b = kv_indptr[b+1] - kv_indptr[b] prefix keys, then
+ *     the T = num_draft draft keys, N_b = P_b + T keys in that order.
+ *     Row (t, h) with t = b*T + i is draft token i of request b, head h.
+ *   - Results are deterministic: identical inputs give bit-identical outputs
+ *     (no atomics in any reduction).
+ */
+#ifndef TVMLA_H
+#define TVMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TVMLA_D_LATENT 512 /* latent width: the value, key entries [0, 512) */
+#define TVMLA_D_ROPE 64    /* rope width: key entries [512, 576)            */
+#define TVMLA_D_KEY 576
+#define TVMLA_MAX_DRAFT 64
+#define TVMLA_MAX_HEADS 128
+#define TVMLA_MAX_NSPLIT 256
+
+typedef enum { TVMLA_BF16 = 0, TVMLA_FP32 = 1 } tvmla_dtype;
+
+typedef enum {
+  TVMLA_OK = 0,
+  TVMLA_E_NULLPTR = 1,   /* a required pointer is NULL                          */
+  TVMLA_E_SHAPE = 2,     /* a size or count is out of range                      */
+  TVMLA_E_DTYPE = 3,     /* unknown dtype, or a dtype the chosen algorithm lacks */
+  TVMLA_E_WORKSPACE = 4, /* workspace NULL or smaller than tvmla_workspace_bytes */
+  TVMLA_E_ALIGN = 5,     /* a pointer or stride breaks the alignment rules       */
+  TVMLA_E_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch             */
+  TVMLA_E_ALGO = 7       /* unknown algorithm selector                           */
+} tvmla_status;
+
+typedef enum {
+  TVMLA_ALGO_AUTO = 0,   /* bf16 -> MFMA kernel, fp32 -> scalar kernel          */
+  TVMLA_ALGO_SCALAR = 1, /* one wavefront per (row, split); fp32 FMA; any dtype */
+  TVMLA_ALGO_MFMA = 2    /* bf16 MFMA kernel; bf16 only                         */
+} tvmla_algo;
+
+/*
+ * Bytes of workspace tvmla_verify needs: the per-split partial results
+ * (page 1, "Assumptions and Their Validity", assumption 3: a fixed
+ * workspace sized from batch and constants only). It depends only on its
+ * arguments, never on sequence lengths. Returns 0 for out-of-range
+ * arguments.
+ *
+ * Layout (fp32, each region 256-byte aligned), R = num_draft*num_heads:
+ *   o_part   [batch][nsplit][R][512]  split s's output, normalised by its
+ *                                     own softmax sum
+ *   lse_part [batch][nsplit][R]       split s's natural-log sum of exp
+ *                                     (-inf when the split sees no key)
+ * Row r = i*num_heads + h. Only splits that hold keys are written; the
+ * rest of the workspace is left as it was.
+ */
+size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit);
+
+/*
+ * Verify attention, then the log-sum-exp combine of its splits.
+ *
+ * q_nope   [batch*num_draft, num_heads, 512] dtype; element (t, h, d) at
+ *          q_nope + t*q_nope_stride_tok + h*q_nope_stride_head + d
+ * q_rope   [batch*num_draft, num_heads, 64] dtype, same form with its own
+ *          strides (a packed [.., .., 576] query passes as two views).
+ *          Strides are in elements; the last dimension is contiguous.
+ * kv_cache [num_slots, kv_stride_row] dtype; row s holds slot s's key:
+ *          entries [0, 512) the latent (also the value), [512, 576) rope.
+ * kv_indptr     int32 [batch+1]   offsets into kv_indices (prefix only)
+ * kv_indices    int32 [kv_indptr[batch]]  cache slots of prefix keys
+ * out_cache_loc int32 [batch*num_draft]   cache slots of draft keys
+ *               (their rows are already written)
+ * custom_mask   uint8, per request a row-major [num_draft][N_b] block at
+ *               offset mask_indptr[b]; nonzero = visible
+ * mask_indptr   int32 [batch+1]
+ * sm_scale      multiplies the full 576-wide dot product
+ * nsplit        splits per request: split s covers keys
+ *               [s*chunk, min((s+1)*chunk, N_b)), chunk = ceil(N_b/nsplit)
+ *               (page 1, "The NSPLIT Calculation"); empty splits return at
+ *               once.
+ * out      [batch*num_draft, num_heads, 512] dtype, contiguous; bf16 output
+ *          is rounded to nearest even
+ * lse      [batch*num_draft, num_heads] fp32, contiguous: natural log of the
+ *          sum of exp(score) over the visible keys. A row that sees no key
+ *          gets out = 0 and lse = -inf.
+ * workspace, workspace_bytes: at least tvmla_workspace_bytes(...) bytes;
+ *          contents on entry are ignored.
+ *
+ * Alignment: q, kv_cache, out and workspace 16-byte aligned; q strides and
+ * kv_stride_row multiples of 16 bytes; kv_stride_row >= 576.
+ * Limits: 1 <= batch; 1 <= num_draft <= 64; 1 <= num_heads <= 128;
+ * 1 <= nsplit <= 256.
+ */
+tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                          const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                          const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* out_cache_loc,
+                          const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                          int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                          int32_t dtype, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * tvmla_verify with two extra knobs:
+ *   algo       a tvmla_algo value (TVMLA_ALGO_AUTO is tvmla_verify's choice)
+ *   min_chunk  lower bound on the per-split chunk: chunk =
+ *              max(ceil(N_b/nsplit), min_chunk). 0 or 1 keeps the rule
+ *              above exactly. A larger value leaves short requests fewer,
+ *              longer splits (the launch is unchanged; surplus splits return
+ *              at once), which cuts partial-result traffic; the result
+ *              differs only by rounding.
+ */
+tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* out_cache_loc,
+                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                             int32_t dtype, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
+
+/*
+ * The combine step alone: merge per-split partials laid out as in
+ * tvmla_workspace_bytes (the reduce of page 1, "The Design Emerges", first
+ * insight). out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse),
+ * lse = max lse + log(sum_s w_s).
+ *
+ * If kv_indptr is non-NULL, split s of request b is read only when it holds
+ * keys under the schedule above (N_b = kv_indptr[b+1]-kv_indptr[b]+num_draft,
+ * chunk = max(ceil(N_b/nsplit), min_chunk)); other splits are never read.
+ * If kv_indptr is NULL every split is read and a split with lse = -inf
+ * weighs nothing. A row whose splits are all -inf gets out = 0, lse = -inf.
+ * workspace: as for tvmla_verify (read only here).
+ */
+tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,
+                           int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit,
+                           int32_t min_chunk, int32_t dtype, void* out, float* lse, void* stream);
+
+/* A static, human-readable name for a status code (host pointer, never NULL). */
+const char* tvmla_status_str(int32_t status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t tvmla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TVMLA_H */

@@ -1,0 +1,170 @@
+"""ctypes binding for libtvmla.so: the same entry points as include/tvmla.h.
+
+Argument marshalling only. Tensors are torch tensors on the GPU (device
+memory and streams are PyTorch's job here); every step of the computation
+runs in the library's HIP kernels. If the library is missing the binding
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtvmla.so")
+
+BF16, FP32 = 0, 1
+ALGO_AUTO, ALGO_SCALAR, ALGO_MFMA = 0, 1, 2
+D_LATENT, D_ROPE, D_KEY = 512, 64, 576
+
+STATUS = {
+    0: "TVMLA_OK",
+    1: "TVMLA_E_NULLPTR",
+    2: "TVMLA_E_SHAPE",
+    3: "TVMLA_E_DTYPE",
+    4: "TVMLA_E_WORKSPACE",
+    5: "TVMLA_E_ALIGN",
+    6: "TVMLA_E_LAUNCH",
+    7: "TVMLA_E_ALGO",
+}
+
+# every symbol include/tvmla.h declares
+EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_combine",
+           "tvmla_status_str", "tvmla_version")
+
+
+class TvmlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_VERIFY_ARGS = [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _I32, _I32,
+                _P, _P, _P, _SZ, _P]
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m speculative_decoding_verify_mla_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.tvmla_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
+    lib.tvmla_workspace_bytes.restype = _SZ
+    lib.tvmla_verify.argtypes = _VERIFY_ARGS
+    lib.tvmla_verify.restype = ctypes.c_int
+    lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32]
+    lib.tvmla_verify_ex.restype = ctypes.c_int
+    lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
+    lib.tvmla_combine.restype = ctypes.c_int
+    lib.tvmla_status_str.argtypes = [_I32]
+    lib.tvmla_status_str.restype = ctypes.c_char_p
+    lib.tvmla_version.argtypes = []
+    lib.tvmla_version.restype = _I32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().tvmla_status_str(status).decode()
+
+
+def version() -> int:
+    return load().tvmla_version()
+
+
+def workspace_bytes(batch: int, num_draft: int, num_heads: int, nsplit: int) -> int:
+    return load().tvmla_workspace_bytes(batch, num_draft, num_heads, nsplit)
+
+
+def _check(status: int):
+    if status != 0:
+        raise TvmlaError(status, status_str(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TvmlaError(3, f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+           sm_scale: float, nsplit: int, out, lse, workspace, num_draft: int,
+           algo: int = ALGO_AUTO, min_chunk: int = 0, stream=None) -> None:
+    """Enqueue tvmla_verify_ex on `stream` (default: torch's current stream).
+
+    q_nope [batch*T, H, 512], q_rope [batch*T, H, 64] (last dim contiguous),
+    kv_cache [slots, >=576] (row-contiguous), int32 metadata, uint8 mask,
+    out [batch*T, H, 512] (q's dtype), lse [batch*T, H] fp32, workspace a
+    byte tensor of at least workspace_bytes(...) bytes.
+    """
+    ntok, H, dl = q_nope.shape
+    if dl != D_LATENT or tuple(q_rope.shape) != (ntok, H, D_ROPE):
+        raise TvmlaError(2, "q_nope must be [tok, H, 512] and q_rope [tok, H, 64]")
+    if q_nope.stride(2) != 1 or q_rope.stride(2) != 1 or kv_cache.stride(1) != 1:
+        raise TvmlaError(5, "last dimensions must be contiguous")
+    if ntok % num_draft:
+        raise TvmlaError(2, "token count must be batch * num_draft")
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise TvmlaError(5, "out and lse must be contiguous")
+    batch = ntok // num_draft
+    dt = _dtype_code(q_nope)
+    if q_rope.dtype != q_nope.dtype or kv_cache.dtype != q_nope.dtype or out.dtype != q_nope.dtype:
+        raise TvmlaError(3, "q_nope, q_rope, kv_cache and out must share one dtype")
+    st = load().tvmla_verify_ex(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0),
+        _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
+        batch, num_draft, H, float(sm_scale), nsplit, dt,
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream), algo, min_chunk)
+    _check(st)
+
+
+def combine(workspace, kv_indptr, batch: int, num_draft: int, num_heads: int, nsplit: int, out, lse,
+            min_chunk: int = 0, stream=None) -> None:
+    """Enqueue tvmla_combine: merge the workspace's split partials into out/lse."""
+    st = load().tvmla_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(kv_indptr),
+                              batch, num_draft, num_heads, nsplit, min_chunk, _dtype_code(out),
+                              _ptr(out), _ptr(lse), _stream_ptr(stream))
+    _check(st)
+
+
+def workspace_views(workspace, batch: int, num_draft: int, num_heads: int, nsplit: int):
+    """The partial-result regions of a workspace as tensors:
+    o_part [batch, nsplit, R, 512] and lse_part [batch, nsplit, R] (fp32)."""
+    import torch
+
+    R = num_draft * num_heads
+    rows = batch * nsplit * R
+    o_bytes = rows * D_LATENT * 4
+    lse_off = (o_bytes + 255) // 256 * 256
+    raw = workspace.view(torch.uint8)
+    o = raw[:o_bytes].view(torch.float32).view(batch, nsplit, R, D_LATENT)
+    lse = raw[lse_off:lse_off + rows * 4].view(torch.float32).view(batch, nsplit, R)
+    return o, lse

@@ -1,0 +1,175 @@
+// C ABI of tvmla: host-side argument checks, workspace carving, launches.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state. A call that passes enqueues exactly
+// two kernels on the caller's stream (split, then combine); the launch
+// configuration depends only on (batch, num_draft, num_heads, nsplit), so
+// the pair can be captured into a hipGraph once and replayed while the
+// metadata buffers change underneath (page 1, "The Core Problem": graph
+// replay reissues the same launches at the same addresses).
+
+#include "../../include/tvmla.h"
+#include "tvmla_internal.h"
+
+using namespace tvmla;
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+tvmla_status check_shape(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
+  if (batch < 1 || batch > 65535) return TVMLA_E_SHAPE;
+  if (num_draft < 1 || num_draft > TVMLA_MAX_DRAFT) return TVMLA_E_SHAPE;
+  if (num_heads < 1 || num_heads > TVMLA_MAX_HEADS) return TVMLA_E_SHAPE;
+  if (nsplit < 1 || nsplit > TVMLA_MAX_NSPLIT) return TVMLA_E_SHAPE;
+  return TVMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
+  if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return 0;
+  return workspace_layout(batch, num_draft, num_heads, nsplit).total;
+}
+
+const char* tvmla_status_str(int32_t status) {
+  switch (status) {
+    case TVMLA_OK: return "ok";
+    case TVMLA_E_NULLPTR: return "a required pointer is NULL";
+    case TVMLA_E_SHAPE: return "a size or count is out of range";
+    case TVMLA_E_DTYPE: return "unsupported dtype for this algorithm";
+    case TVMLA_E_WORKSPACE: return "workspace missing or too small";
+    case TVMLA_E_ALIGN: return "pointer or stride misaligned";
+    case TVMLA_E_LAUNCH: return "kernel launch failed";
+    case TVMLA_E_ALGO: return "unknown algorithm";
+    default: return "unknown status";
+  }
+}
+
+int32_t tvmla_version(void) { return 100; /* 0.1.0 */ }
+
+tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* out_cache_loc,
+                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                             int32_t dtype, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+  if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
+  if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA) return TVMLA_E_ALGO;
+  if (algo == TVMLA_ALGO_AUTO) algo = dtype == TVMLA_BF16 ? TVMLA_ALGO_MFMA : TVMLA_ALGO_SCALAR;
+  if (algo == TVMLA_ALGO_MFMA && dtype != TVMLA_BF16) return TVMLA_E_DTYPE;
+  if (!q_nope || !q_rope || !kv_cache || !kv_indptr || !kv_indices || !out_cache_loc || !custom_mask ||
+      !mask_indptr || !out || !lse)
+    return TVMLA_E_NULLPTR;
+  if (!workspace) return TVMLA_E_WORKSPACE;
+  tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
+  if (st != TVMLA_OK) return st;
+  if (min_chunk < 0) return TVMLA_E_SHAPE;
+  if (kv_stride_row < TVMLA_D_KEY) return TVMLA_E_SHAPE;
+  if (q_nope_stride_tok < 0 || q_nope_stride_head < 0 || q_rope_stride_tok < 0 || q_rope_stride_head < 0)
+    return TVMLA_E_SHAPE;
+  const int64_t esz = dtype == TVMLA_BF16 ? 2 : 4;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(out) || !aligned16(workspace))
+    return TVMLA_E_ALIGN;
+  if ((kv_stride_row * esz) % 16 || (q_nope_stride_tok * esz) % 16 || (q_nope_stride_head * esz) % 16 ||
+      (q_rope_stride_tok * esz) % 16 || (q_rope_stride_head * esz) % 16)
+    return TVMLA_E_ALIGN;
+  const WorkspaceLayout wl = workspace_layout(batch, num_draft, num_heads, nsplit);
+  if (workspace_bytes < wl.total) return TVMLA_E_WORKSPACE;
+
+  SplitParams p;
+  p.q_nope = q_nope;
+  p.qn_stride_tok = q_nope_stride_tok;
+  p.qn_stride_head = q_nope_stride_head;
+  p.q_rope = q_rope;
+  p.qr_stride_tok = q_rope_stride_tok;
+  p.qr_stride_head = q_rope_stride_head;
+  p.kv = kv_cache;
+  p.kv_stride = kv_stride_row;
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  p.out_cache_loc = out_cache_loc;
+  p.mask = custom_mask;
+  p.mask_indptr = mask_indptr;
+  p.batch = batch;
+  p.num_draft = num_draft;
+  p.num_heads = num_heads;
+  p.nsplit = nsplit;
+  p.min_chunk = min_chunk;
+  p.sm_scale = sm_scale;
+  char* ws = static_cast<char*>(workspace);
+  p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
+  p.lse_part = reinterpret_cast<float*>(ws + wl.lse_off);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (algo == TVMLA_ALGO_MFMA)
+    e = launch_split_mfma_bf16(p, s);
+  else if (dtype == TVMLA_BF16)
+    e = launch_split_scalar_bf16(p, s);
+  else
+    e = launch_split_scalar_fp32(p, s);
+  if (e != hipSuccess) return TVMLA_E_LAUNCH;
+
+  CombineParams c;
+  c.o_part = p.o_part;
+  c.lse_part = p.lse_part;
+  c.kv_indptr = kv_indptr;
+  c.batch = batch;
+  c.num_draft = num_draft;
+  c.num_heads = num_heads;
+  c.nsplit = nsplit;
+  c.min_chunk = min_chunk;
+  c.out = out;
+  c.lse = lse;
+  if (launch_combine(c, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
+tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                          const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                          const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* out_cache_loc,
+                          const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                          int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                          int32_t dtype, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return tvmla_verify_ex(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
+                         q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
+                         custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out,
+                         lse, workspace, workspace_bytes, stream, TVMLA_ALGO_AUTO, 0);
+}
+
+tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,
+                           int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit,
+                           int32_t min_chunk, int32_t dtype, void* out, float* lse, void* stream) {
+  if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
+  if (!out || !lse) return TVMLA_E_NULLPTR;
+  if (!workspace) return TVMLA_E_WORKSPACE;
+  tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
+  if (st != TVMLA_OK) return st;
+  if (min_chunk < 0) return TVMLA_E_SHAPE;
+  if (!aligned16(workspace) || !aligned16(out)) return TVMLA_E_ALIGN;
+  const WorkspaceLayout wl = workspace_layout(batch, num_draft, num_heads, nsplit);
+  if (workspace_bytes < wl.total) return TVMLA_E_WORKSPACE;
+  const char* ws = static_cast<const char*>(workspace);
+  CombineParams c;
+  c.o_part = reinterpret_cast<const float*>(ws + wl.o_off);
+  c.lse_part = reinterpret_cast<const float*>(ws + wl.lse_off);
+  c.kv_indptr = kv_indptr;
+  c.batch = batch;
+  c.num_draft = num_draft;
+  c.num_heads = num_heads;
+  c.nsplit = nsplit;
+  c.min_chunk = min_chunk;
+  c.out = out;
+  c.lse = lse;
+  if (launch_combine(c, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Internal declarations shared by the tvmla kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tvmla {
+
+constexpr int kDLatent = 512;
+constexpr int kDRope = 64;
+constexpr int kDKey = kDLatent + kDRope;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything a split kernel needs; passed by value as one kernel argument.
+struct SplitParams {
+  const void* q_nope;
+  int64_t qn_stride_tok, qn_stride_head;  // elements
+  const void* q_rope;
+  int64_t qr_stride_tok, qr_stride_head;  // elements
+  const void* kv;
+  int64_t kv_stride;  // elements per cache row
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* out_cache_loc;
+  const uint8_t* mask;
+  const int32_t* mask_indptr;
+  int32_t batch, num_draft, num_heads, nsplit, min_chunk;
+  float sm_scale;
+  float* o_part;    // [batch][nsplit][R][512]
+  float* lse_part;  // [batch][nsplit][R]
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* kv_indptr;  // may be null: read every split
+  int32_t batch, num_draft, num_heads, nsplit, min_chunk;
+  void* out;
+  float* lse;
+};
+
+// Workspace regions (byte offsets from the workspace base).
+struct WorkspaceLayout {
+  size_t o_off, lse_off, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_draft, int64_t num_heads, int64_t nsplit) {
+  const size_t rows = (size_t)batch * (size_t)nsplit * (size_t)num_draft * (size_t)num_heads;
+  WorkspaceLayout w;
+  w.o_off = 0;
+  w.lse_off = align_up(rows * kDLatent * sizeof(float), 256);
+  w.total = align_up(w.lse_off + rows * sizeof(float), 256);
+  return w;
+}
+
+// Key range [start, end) of split s of a request with n keys: chunk =
+// max(ceil(n / nsplit), min_chunk), split s starts at s * chunk.
+__host__ __device__ inline void split_bounds(int n, int nsplit, int min_chunk, int s, int& start, int& end) {
+  int chunk = (n + nsplit - 1) / nsplit;
+  if (chunk < min_chunk) chunk = min_chunk;
+  const int64_t st = (int64_t)s * chunk;
+  start = st < n ? (int)st : n;
+  const int64_t en = st + chunk;
+  end = en < n ? (int)en : n;
+}
+
+// Number of leading splits that hold keys under split_bounds.
+__host__ __device__ inline int active_splits(int n, int nsplit, int min_chunk) {
+  if (n <= 0) return 0;
+  int chunk = (n + nsplit - 1) / nsplit;
+  if (chunk < min_chunk) chunk = min_chunk;
+  const int a = (n + chunk - 1) / chunk;
+  return a < nsplit ? a : nsplit;
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_split_scalar_bf16(const SplitParams& p, hipStream_t stream);
+hipError_t launch_split_scalar_fp32(const SplitParams& p, hipStream_t stream);
+hipError_t launch_split_mfma_bf16(const SplitParams& p, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& c, int dtype, hipStream_t stream);
+
+}  // namespace tvmla

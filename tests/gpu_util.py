@@ -1,0 +1,86 @@
+"""Helpers for the GPU tests: run the HIP path on a workload, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from speculative_decoding_verify_mla_amd import binding
+
+# bf16 outputs: |gpu - oracle| <= 2e-2 + 2e-2 |oracle|; fp32 lse: 1e-3 absolute.
+BF16_ATOL, BF16_RTOL, BF16_LSE = 2e-2, 2e-2, 1e-3
+# fp32 outputs: fp32 accumulation of 576-term dot products and of the softmax
+# sum keeps errors near 1e-6; 1e-4 leaves a wide margin and still catches any
+# dropped term or wrong index.
+FP32_ATOL, FP32_RTOL, FP32_LSE = 1e-4, 1e-4, 1e-4
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class Device:
+    """A workload resident on the GPU, ready for repeated verify calls."""
+
+    def __init__(self, w, nsplit=None, fill=float("nan"), row_stride=576):
+        self.w = w
+        dev = "cuda"
+        self.nsplit = nsplit or w.spec.nsplit
+        self.pool = w.device_pool(dev, fill=fill, row_stride=row_stride)
+        self.q_nope = w.q_nope.to(dev)
+        self.q_rope = w.q_rope.to(dev)
+        self.kv_indptr = w.kv_indptr.to(dev)
+        self.kv_indices = w.kv_indices.to(dev) if w.kv_indices.numel() else torch.zeros(1, dtype=torch.int32,
+                                                                                         device=dev)
+        self.out_cache_loc = w.out_cache_loc.to(dev)
+        self.custom_mask = w.custom_mask.to(dev)
+        self.mask_indptr = w.mask_indptr.to(dev)
+        ntok, H = w.q_nope.shape[0], w.num_heads
+        self.out = torch.full((ntok, H, 512), float("nan"), dtype=w.torch_dtype, device=dev)
+        self.lse = torch.full((ntok, H), float("nan"), dtype=torch.float32, device=dev)
+        nbytes = binding.workspace_bytes(w.batch, w.num_draft, H, self.nsplit)
+        self.ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=dev)
+
+    def run(self, algo=binding.ALGO_AUTO, min_chunk=0, nsplit=None, stream=None):
+        ns = nsplit or self.nsplit
+        if ns != self.nsplit:
+            nbytes = binding.workspace_bytes(self.w.batch, self.w.num_draft, self.w.num_heads, ns)
+            if self.ws.numel() * 4 < nbytes:
+                self.ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        binding.verify(self.q_nope, self.q_rope, self.pool[:, :576] if self.pool.shape[1] != 576 else self.pool,
+                       self.kv_indptr, self.kv_indices, self.out_cache_loc, self.custom_mask, self.mask_indptr,
+                       self.w.sm_scale, ns, self.out, self.lse, self.ws, self.w.num_draft, algo=algo,
+                       min_chunk=min_chunk, stream=stream)
+        return self.out, self.lse
+
+    def result(self, **kw):
+        out, lse = self.run(**kw)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def tolerances(w):
+    if w.spec.dtype == "bf16":
+        return BF16_ATOL, BF16_RTOL, BF16_LSE
+    return FP32_ATOL, FP32_RTOL, FP32_LSE
+
+
+def compare(w, out, lse, ref_out, ref_lse, what=""):
+    """Element-wise check against the oracle; also logs max-abs, max-rel, rel-L2."""
+    atol, rtol, ltol = tolerances(w)
+    err = np.abs(out - ref_out)
+    bound = atol + rtol * np.abs(ref_out)
+    lerr = np.abs(lse - ref_lse)
+    l2 = float(np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-300))
+    log(f"  {what}: max|err| out {err.max():.3e} (worst err/bound {np.max(err / bound):.3f}), "
+        f"lse {np.nanmax(lerr) if lerr.size else 0:.3e}, rel-L2 {l2:.3e}")
+    assert np.all(np.isfinite(out)), "non-finite output"
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} outputs outside tolerance, max err {err.max()}"
+    same_inf = np.isneginf(lse) == np.isneginf(ref_lse)
+    assert same_inf.all(), f"{what}: -inf lse pattern differs"
+    fin = np.isfinite(ref_lse)
+    assert np.all(lerr[fin] <= ltol), f"{what}: lse max err {lerr[fin].max()}"
+    return l2

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/tvmla.h declares, sizes its workspace as documented, and rejects bad
+arguments on the host before any HIP call (so these run on a GPU-less box)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_verify_mla_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tvmla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from speculative_decoding_verify_mla_amd import build
+
+        build.build()
+    return binding.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tvmla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert _declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_version_and_status_strings(lib):
+    assert binding.version() >= 100
+    for code in range(8):
+        s = binding.status_str(code)
+        assert isinstance(s, str) and s
+    assert binding.status_str(99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    # fp32 partials: 512-wide output + lse per (token, head, split), 256-byte aligned regions
+    bs, T, H, ns = 8, 9, 64, 64
+    rows = bs * T * H * ns
+    o = rows * 512 * 4
+    expect = o + ((rows * 4 + 255) // 256) * 256
+    assert binding.workspace_bytes(bs, T, H, ns) == expect
+    # the pages' figure: about 600 MB at batch 8, 9 draft tokens, NSPLIT 64 (64 heads)
+    assert abs(expect - 600e6) < 0.05 * 600e6
+    # a pure function of its arguments; rejects out-of-range ones
+    assert binding.workspace_bytes(1, 16, 64, 64) == binding.workspace_bytes(1, 16, 64, 64)
+    for bad in [(0, 1, 1, 1), (1, 0, 1, 1), (1, 65, 1, 1), (1, 1, 0, 1), (1, 1, 129, 1), (1, 1, 1, 0),
+                (1, 1, 1, 257)]:
+        assert binding.workspace_bytes(*bad) == 0
+
+
+# ---------------------------------------------------------------- error paths
+
+_FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case fails a host check first
+
+
+def _call(lib, **kw):
+    a = dict(q_nope=_FAKE, qn_st=64 * 512, qn_sh=512, q_rope=_FAKE, qr_st=64 * 64, qr_sh=64, kv=_FAKE,
+             kv_stride=576, kv_indptr=_FAKE, kv_indices=_FAKE, ocl=_FAKE, mask=_FAKE, mask_indptr=_FAKE,
+             batch=1, T=4, H=64, scale=0.07, nsplit=64, dtype=binding.BF16, out=_FAKE, lse=_FAKE,
+             ws=_FAKE, ws_bytes=None, stream=None, algo=0, min_chunk=0)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = binding.workspace_bytes(max(a["batch"], 1), max(min(a["T"], 64), 1),
+                                                max(min(a["H"], 128), 1), max(min(a["nsplit"], 256), 1))
+    return lib.tvmla_verify_ex(a["q_nope"], a["qn_st"], a["qn_sh"], a["q_rope"], a["qr_st"], a["qr_sh"], a["kv"],
+                               a["kv_stride"], a["kv_indptr"], a["kv_indices"], a["ocl"], a["mask"],
+                               a["mask_indptr"], a["batch"], a["T"], a["H"], a["scale"], a["nsplit"], a["dtype"],
+                               a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"], a["algo"],
+                               a["min_chunk"])
+
+
+@pytest.mark.parametrize("field", ["q_nope", "q_rope", "kv", "kv_indptr", "kv_indices", "ocl", "mask",
+                                   "mask_indptr", "out", "lse"])
+def test_null_pointer(lib, field):
+    assert _call(lib, **{field: None}) == 1
+
+
+def test_null_workspace(lib):
+    assert _call(lib, ws=None) == 4
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(batch=70000), dict(T=0), dict(T=65), dict(H=0), dict(H=129),
+                                dict(nsplit=0), dict(nsplit=257), dict(min_chunk=-1), dict(kv_stride=575),
+                                dict(qn_st=-512)])
+def test_bad_shape(lib, kw):
+    assert _call(lib, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1), dict(dtype=binding.FP32, algo=binding.ALGO_MFMA)])
+def test_bad_dtype(lib, kw):
+    assert _call(lib, **kw) == 3
+
+
+def test_bad_algo(lib):
+    assert _call(lib, algo=3) == 7
+
+
+@pytest.mark.parametrize("kw", [dict(q_nope=_FAKE + 8), dict(kv=_FAKE + 2), dict(out=_FAKE + 4), dict(ws=_FAKE + 8),
+                                dict(kv_stride=580), dict(qn_sh=516), dict(qr_st=64 * 64 + 4)])
+def test_misaligned(lib, kw):
+    assert _call(lib, **kw) == 5
+
+
+def test_small_workspace(lib):
+    need = binding.workspace_bytes(1, 4, 64, 64)
+    assert _call(lib, ws_bytes=need - 1) == 4
+
+
+def test_combine_errors(lib):
+    f = lib.tvmla_combine
+    ws = binding.workspace_bytes(1, 4, 64, 64)
+    assert f(_FAKE, ws, _FAKE, 1, 4, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
+    assert f(_FAKE, ws, _FAKE, 1, 4, 64, 64, 0, 0, None, _FAKE, None) == 1
+    assert f(None, ws, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    assert f(_FAKE, ws - 1, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    assert f(_FAKE, ws, _FAKE, 0, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 2
+    assert f(_FAKE + 4, ws, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(FileNotFoundError):
+        binding.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and medium workloads are compared element by element on every output;
+the full-size long-context, ragged and heavy workloads on sampled rows the
+oracle computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import verify_fp64 as vo
+from speculative_decoding_verify_mla_amd import binding
+from tests.gpu_util import Device, compare, log
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+MFMA, SCALAR = binding.ALGO_MFMA, binding.ALGO_SCALAR
+
+
+def _oracle(w, pool=None):
+    pool = w.host_pool() if pool is None else pool
+    return vo.verify(w.q_nope, w.q_rope, pool, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
+                     w.mask_indptr, w.sm_scale, w.num_draft)
+
+
+def _oracle_rows(w, picks, pool=None):
+    pool = w.host_pool() if pool is None else pool
+    return vo.verify_rows(w.q_nope, w.q_rope, pool, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
+                          w.mask_indptr, w.sm_scale, w.num_draft, picks)
+
+
+def _algos(w):
+    return [SCALAR] if w.spec.dtype == "fp32" else [MFMA, SCALAR]
+
+
+SMALL = {
+    # multiple tiles, ragged tails, a partial 128-row group (8 heads x 5 tokens)
+    "ragged_h8": gen.small("ragged_h8", 3, [0, 37, 300], 5, 8, seed=11),
+    # eight full row groups per request, many splits of a few keys
+    "groups_h64": gen.small("groups_h64", 2, [200, 1000], 16, 64, seed=12),
+    # degenerate: one token, one head; the second request has no prefix at all
+    "t1_h1": gen.small("t1_h1", 2, [5, 0], 1, 1, seed=13),
+    # largest tree, two heads
+    "t64_h2": gen.small("t64_h2", 1, [100], 64, 2, seed=14),
+    # largest head count
+    "t2_h128": gen.small("t2_h128", 1, [50], 2, 128, seed=15),
+    # chain tree over a longer prefix
+    "chain_h16": gen.small("chain_h16", 2, [700, 65], 8, 16, tree="chain", seed=16),
+    # fp32 through the scalar kernel, ragged
+    "fp32_ragged": gen.small("fp32_ragged", 3, [0, 9, 130], 4, 8, dtype="fp32", seed=17),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", "p4096"])
+def test_named_configs_full(name):
+    w = gen.build(name)
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w)
+    for algo in _algos(w):
+        log(f"[{name}] algo={algo} batch={w.batch} T={w.num_draft} H={w.num_heads} P={list(w.prefix_lens)}")
+        out, lse = d.result(algo=algo)
+        compare(w, out, lse, ref_out, ref_lse, f"{name}/algo{algo}")
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_cases_full(name):
+    w = gen.build(SMALL[name])
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w)
+    for algo in _algos(w):
+        log(f"[{name}] algo={algo}")
+        out, lse = d.result(algo=algo)
+        compare(w, out, lse, ref_out, ref_lse, f"{name}/algo{algo}")
+
+
+@pytest.mark.parametrize("nsplit", [1, 3, 64, 200])
+def test_nsplit_invariance(nsplit):
+    w = gen.build("p4096")
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w, nsplit=nsplit)
+    log(f"[p4096] nsplit={nsplit}")
+    out, lse = d.result(algo=MFMA)
+    compare(w, out, lse, ref_out, ref_lse, f"nsplit{nsplit}")
+
+
+@pytest.mark.parametrize("min_chunk", [16, 256, 100000])
+def test_min_chunk(min_chunk):
+    w = gen.build(SMALL["groups_h64"])
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w)
+    for algo in (MFMA, SCALAR):
+        out, lse = d.result(algo=algo, min_chunk=min_chunk)
+        compare(w, out, lse, ref_out, ref_lse, f"min_chunk{min_chunk}/algo{algo}")
+
+
+def test_partials_match_oracle_splits():
+    """The workspace after a call holds each split's (normalised output, lse),
+    matching the oracle's per-split attention on the pages' schedule."""
+    w = gen.build(SMALL["ragged_h8"])
+    ns = 7
+    pool = w.host_pool()
+    o_ref, l_ref, nonempty = vo.verify_partials(w.q_nope, w.q_rope, pool, w.kv_indptr, w.kv_indices,
+                                                w.out_cache_loc, w.custom_mask, w.mask_indptr, w.sm_scale,
+                                                w.num_draft, ns)
+    d = Device(w, nsplit=ns)
+    T, H = w.num_draft, w.num_heads
+    for algo in (MFMA, SCALAR):
+        d.ws.fill_(float("nan"))
+        d.result(algo=algo)
+        o_ws, l_ws = binding.workspace_views(d.ws, w.batch, T, H, ns)
+        o_ws, l_ws = o_ws.cpu().numpy().astype(np.float64), l_ws.cpu().numpy().astype(np.float64)
+        for b in range(w.batch):
+            for s in range(ns):
+                got_o = o_ws[b, s].reshape(T, H, 512)
+                got_l = l_ws[b, s].reshape(T, H)
+                if not nonempty[b, s]:
+                    assert np.isnan(got_l).all(), "an empty split wrote to the workspace"
+                    continue
+                ro = o_ref[b * T:(b + 1) * T, :, s]
+                rl = l_ref[b * T:(b + 1) * T, :, s]
+                assert (np.isneginf(got_l) == np.isneginf(rl)).all()
+                fin = np.isfinite(rl)
+                assert np.all(np.abs(got_l[fin] - rl[fin]) <= 1e-3)
+                assert np.all(np.abs(got_o - ro) <= 2e-2 + 2e-2 * np.abs(ro)), (b, s)
+
+
+def test_combine_entry_point():
+    """tvmla_combine on synthetic partials (some splits at -inf, one row all -inf)."""
+    batch, T, H, ns = 2, 3, 4, 5
+    g = torch.Generator().manual_seed(3)
+    nbytes = binding.workspace_bytes(batch, T, H, ns)
+    ws = torch.zeros(nbytes // 4, dtype=torch.float32)
+    o_v, l_v = binding.workspace_views(ws, batch, T, H, ns)
+    o_v.copy_(torch.randn(o_v.shape, generator=g))
+    l_v.copy_(torch.randn(l_v.shape, generator=g) * 3)
+    l_v[0, 1] = float("-inf")
+    l_v[1, :, 5] = float("-inf")
+    o_ref = o_v.permute(0, 2, 1, 3).reshape(batch * T, H, ns, 512).numpy()
+    l_ref = l_v.permute(0, 2, 1).reshape(batch * T, H, ns).numpy()
+    ref_out, ref_lse = vo.combine(o_ref, l_ref)
+    wsd = ws.cuda()
+    for dt, tol in ((torch.float32, 1e-5), (torch.bfloat16, 1e-2)):
+        out = torch.full((batch * T, H, 512), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((batch * T, H), float("nan"), device="cuda")
+        binding.combine(wsd, None, batch, T, H, ns, out, lse)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        assert np.all(np.abs(o - ref_out) <= tol + tol * np.abs(ref_out))
+        lg = lse.cpu().numpy()
+        assert (np.isneginf(lg) == np.isneginf(ref_lse)).all()
+        fin = np.isfinite(ref_lse)
+        assert np.all(np.abs(lg[fin] - ref_lse[fin]) <= 1e-5)
+        assert np.all(o[~fin] == 0)
+
+
+def test_deterministic_and_poison_free():
+    w = gen.build(SMALL["groups_h64"])
+    d = Device(w)
+    for algo in (MFMA, SCALAR):
+        o1, l1 = d.result(algo=algo)
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.ws.fill_(float("nan"))
+        for _ in range(5):
+            o2, l2 = d.result(algo=algo)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_slot_layout_bitwise():
+    """Scattered vs contiguous slots (and a padded cache row stride): same bits."""
+    a = gen.build(gen.small("lay", 2, [333, 70], 8, 16, seed=21))
+    b = gen.build(gen.small("lay", 2, [333, 70], 8, 16, seed=21, layout="contiguous"))
+    assert not np.array_equal(a.slots, b.slots)
+    da, db, dp = Device(a), Device(b), Device(a, row_stride=640)
+    for algo in (MFMA, SCALAR):
+        oa, la = da.result(algo=algo)
+        ob, lb = db.result(algo=algo)
+        op, lp = dp.result(algo=algo)
+        assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+        assert np.array_equal(oa, op) and np.array_equal(la, lp)
+
+
+def test_masked_content_independence():
+    w = gen.build(gen.small("mask", 1, [150], 12, 8, seed=31))
+    d = Device(w)
+    T, P, H = w.num_draft, int(w.prefix_lens[0]), w.num_heads
+    N = P + T
+    vis = w.custom_mask.reshape(T, N).numpy() != 0
+    leaf = max(range(T), key=lambda j: -vis[:, P + j].sum())  # seen by the fewest tokens
+    for algo in (MFMA, SCALAR):
+        o1, l1 = d.result(algo=algo)
+        saved = d.pool[int(w.out_cache_loc[leaf])].clone()
+        d.pool[int(w.out_cache_loc[leaf])] = 37.0
+        o2, l2 = d.result(algo=algo)
+        d.pool[int(w.out_cache_loc[leaf])] = saved
+        for i in range(T):
+            rows = slice(i, i + 1)
+            if not vis[i, P + leaf]:
+                assert np.array_equal(o1[rows], o2[rows]) and np.array_equal(l1[rows], l2[rows])
+            else:
+                assert not np.array_equal(o1[rows], o2[rows])
+
+
+def _picks(w, per_request, seed=0):
+    rng = np.random.default_rng(seed)
+    T, H = w.num_draft, w.num_heads
+    picks = []
+    for b in range(w.batch):
+        cand = [(0, 0), (T - 1, H - 1)] + [(int(rng.integers(T)), int(rng.integers(H))) for _ in range(per_request)]
+        picks += [(b * T + i, h) for i, h in cand[:per_request]]
+    return picks
+
+
+def _convex_bounds(d, w, out):
+    """Each output entry is a convex combination of the visible values, so it
+    lies within [min, max] of the request's 512 latent entries (any size)."""
+    for b in range(w.batch):
+        lo_hi = []
+        sl = slice(int(w.row_offsets[b]), int(w.row_offsets[b + 1]))
+        rows = w.rows[sl][:, :512].cuda().float()
+        lo, hi = rows.min(0).values, rows.max(0).values
+        o = out[b * w.num_draft:(b + 1) * w.num_draft].float()
+        slack = 2e-2 + 2e-2 * torch.maximum(lo.abs(), hi.abs())
+        assert torch.all(o >= lo - slack) and torch.all(o <= hi + slack), b
+        del lo_hi
+
+
+@pytest.mark.parametrize("name,per_request", [("long185k", 24), ("ragged32", 2), ("heavy200k", 3)])
+def test_full_size_sampled(name, per_request):
+    w = gen.build(name)
+    log(f"[{name}] built: batch={w.batch} keys={w.total_keys}")
+    d = Device(w)
+    out, lse = d.run(algo=binding.ALGO_AUTO)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    _convex_bounds(d, w, out)
+    picks = _picks(w, per_request)
+    pool = w.host_pool()
+    ref_o, ref_l = _oracle_rows(w, picks, pool)
+    got_o = np.stack([out[t, h].float().cpu().numpy() for t, h in picks]).astype(np.float64)
+    got_l = np.array([float(lse[t, h]) for t, h in picks])
+    compare(w, got_o, got_l, ref_o, ref_l, f"{name} sampled {len(picks)} rows")
+    if name == "heavy200k":
+        c = gen.build("heavy200k_contig")
+        dc = Device(c)
+        oc, lc = dc.run(algo=binding.ALGO_AUTO)
+        torch.cuda.synchronize()
+        assert torch.equal(out, oc) and torch.equal(lse, lc), "scattered and contiguous slots differ"
+
+
+def test_graph_capture_replay():
+    """Capture one call, then change prefix lengths, trees and masks in place
+    (same buffers, same capacity) and replay: every replay matches the oracle
+    and the eager call."""
+    T, H, ns = 8, 16, 64
+    specs = [gen.small("cap", 2, [300, 500], T, H, seed=41), gen.small("cap", 2, [450, 120], T, H, seed=42),
+             gen.small("cap", 2, [1, 799], T, H, tree="chain", seed=43)]
+    ws_list = [gen.build(s) for s in specs]
+    cap_idx = max(x.kv_indices.numel() for x in ws_list)
+    cap_mask = max(x.custom_mask.numel() for x in ws_list)
+    base = ws_list[0]
+    d = Device(base)
+    kv_indices = torch.zeros(cap_idx, dtype=torch.int32, device="cuda")
+    mask = torch.zeros(cap_mask, dtype=torch.uint8, device="cuda")
+
+    def load(x):
+        kv_indices[:x.kv_indices.numel()].copy_(x.kv_indices.cuda())
+        mask[:x.custom_mask.numel()].copy_(x.custom_mask.cuda())
+        d.kv_indptr.copy_(x.kv_indptr.cuda())
+        d.mask_indptr.copy_(x.mask_indptr.cuda())
+        d.out_cache_loc.copy_(x.out_cache_loc.cuda())
+        d.q_nope.copy_(x.q_nope.cuda())
+        d.q_rope.copy_(x.q_rope.cuda())
+        d.pool[torch.from_numpy(x.slots).cuda()] = x.rows.cuda()
+
+    d.kv_indices, d.custom_mask = kv_indices, mask
+    load(base)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        d.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        d.run()
+    for rep in range(2):
+        for x in ws_list:
+            load(x)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            go, gl = d.out.float().cpu().numpy().astype(np.float64), d.lse.cpu().numpy().astype(np.float64)
+            ro, rl = _oracle(x, d.pool.cpu())
+            compare(x, go, gl, ro, rl, f"replay{rep}/P={list(x.prefix_lens)}")
+            eo, el = d.result()  # eager, same buffers
+            assert np.array_equal(go, eo) and np.array_equal(gl, el)
