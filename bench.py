@@ -1,0 +1,201 @@
+"""Benchmark: tree-verify attention over an MLA latent cache at 185k context.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long185k]
+
+One step = one tvmla_verify call (split kernel + combine kernel) over the
+whole synthetic batch, inputs resident in HBM. Prints ONE JSON line:
+value = effective KV-read GB/s (cache-row bytes the call must read / time per
+call), plus us per call, the split kernel's MFMA roofline fraction (timed
+live with HIP events through tvmla_verify_partials on the same stream), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "us per verify call + effective KV-read GB/s (% HBM peak) at 185k ctx"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FLOP_PER_ROW_KEY = 2 * 576 + 2 * 512  # QK over the 576-wide key + PV over the 512-wide latent
+
+
+def algorithmic(w):
+    """Algorithmic bytes and flops of one verify call on workload w."""
+    keys = w.total_keys
+    T, H = w.num_draft, w.num_heads
+    esz = 2 if w.spec.dtype == "bf16" else 4
+    kv_bytes = keys * 576 * esz
+    meta_bytes = int(w.kv_indices.numel()) * 4 + w.batch * T * 4 + int(w.custom_mask.numel())
+    q_bytes = w.batch * T * H * 576 * esz
+    out_bytes = w.batch * T * H * (512 * esz + 4)
+    flops = FLOP_PER_ROW_KEY * T * H * keys
+    return dict(kv_bytes=kv_bytes, all_bytes=kv_bytes + meta_bytes + q_bytes + out_bytes, flops=flops)
+
+
+def cpu_baseline(w, pool_host, seconds_hint=10.0):
+    """Time the fp64 oracle on a row sample of the same workload (all heads of
+    the first draft tokens), scaled to the whole job's KV-read GB/s."""
+    import numpy as np
+
+    from oracle import verify_fp64 as vo
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the OMP setting
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    T, H = w.num_draft, w.num_heads
+    tokens = min(2, T)
+    picks = [(i, h) for i in range(tokens) for h in range(H)]
+    t0 = time.perf_counter()
+    vo.verify_rows(w.q_nope, w.q_rope, pool_host, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
+                   w.mask_indptr, w.sm_scale, T, picks)
+    dt = time.perf_counter() - t0
+    frac = len(picks) / float(w.batch * T * H)
+    kv = algorithmic(w)["kv_bytes"]
+    return {
+        "value": kv * frac / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle.verify_rows on {len(picks)} of {w.batch * T * H} query rows "
+                  f"(draft tokens 0-{tokens - 1}, all {H} heads, request 0) in {dt:.2f} s; "
+                  f"value = KV bytes x {frac:.4f} / time",
+        "seconds": dt,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long185k")
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
+    ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify path shards by heads or requests with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from speculative_decoding_verify_mla_amd import binding
+    from workloads import gen
+
+    binding.load()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    w = gen.build(args.workload)
+    T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
+    pool = w.device_pool(dev, fill=0.0)
+    kv = pool
+    q_nope, q_rope = w.q_nope.to(dev), w.q_rope.to(dev)
+    kv_indptr, kv_indices = w.kv_indptr.to(dev), w.kv_indices.to(dev)
+    ocl, mask, mask_indptr = w.out_cache_loc.to(dev), w.custom_mask.to(dev), w.mask_indptr.to(dev)
+    ntok = w.batch * T
+    out = torch.empty((ntok, H, 512), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((ntok, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.workspace_bytes(w.batch, T, H, ns), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.verify(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out, lse,
+                       ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
+
+    def split_only():
+        binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns,
+                                ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
+
+    def combine_only():
+        binding.combine(ws, kv_indptr, w.batch, T, H, ns, out, lse, min_chunk=args.min_chunk, stream=stream)
+
+    def timed(fn, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k  # ms
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: warmup done", file=sys.stderr, flush=True)
+    ms_step = timed(step, args.steps)
+    ms_split = timed(split_only, args.steps)
+    ms_combine = timed(combine_only, args.steps)
+    assert torch.isfinite(lse).all(), "non-finite lse"
+    print(f"[bench] step {ms_step * 1e3:.1f} us, split {ms_split * 1e3:.1f} us, combine {ms_combine * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    alg = algorithmic(w)
+    kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
+    split_tflops = alg["flops"] / (ms_split * 1e-3) / 1e12
+    # the split kernel is MFMA-bound when its flops per KV byte exceed the
+    # ridge point (peak flops / peak bandwidth), HBM-bound otherwise
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if alg["flops"] / alg["kv_bytes"] >= ridge:
+        roof = dict(bound="mfma", achieved=round(split_tflops, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(split_tflops / MFMA_BF16_PEAK_TFLOPS, 4))
+    else:
+        split_gbs = alg["all_bytes"] / (ms_split * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(split_gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(split_gbs / HBM_PEAK_GBS, 4))
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_call": round(ms_step * 1e3, 2),
+        "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": w.batch,
+            "prefix": int(w.prefix_lens[0]) if len(set(w.prefix_lens.tolist())) == 1 else "ragged",
+            "num_draft": T,
+            "num_heads": H,
+            "nsplit": ns,
+            "min_chunk": args.min_chunk,
+            "pool_slots": w.spec.pool_slots,
+            "layout": w.spec.layout,
+            "kv_bytes": alg["kv_bytes"],
+            "flops": alg["flops"],
+        },
+        "kernels_us": {"split": round(ms_split * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
+        "roofline": dict(roof, kernel="split", traffic=None),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        host_pool = w.host_pool(fill=0.0)
+        res["cpu_baseline"] = cpu_baseline(w, host_pool)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

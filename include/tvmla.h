@@ -152,6 +152,24 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
                              size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
 
 /*
+ * The split step alone: the same arguments as tvmla_verify_ex without out
+ * and lse. It enqueues only the split kernel, which leaves every non-empty
+ * split's partial result in the workspace (layout under
+ * tvmla_workspace_bytes); tvmla_combine with the same kv_indptr, nsplit and
+ * min_chunk then produces exactly what tvmla_verify_ex does. Callers that
+ * merge partials from several sources, or that time the two steps apart,
+ * use the pair.
+ */
+tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                   const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                   const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                   const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                   const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                                   int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                                   int32_t algo, int32_t min_chunk);
+
+/*
  * The combine step alone: merge per-split partials laid out as in
  * tvmla_workspace_bytes (the reduce of page 1, "The Design Emerges", first
  * insight). out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse),

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     load,
     status_str,
     verify,
+    verify_partials,
     version,
     workspace_bytes,
     workspace_views,

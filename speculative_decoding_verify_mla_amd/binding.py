@@ -30,8 +30,8 @@ STATUS = {
 }
 
 # every symbol include/tvmla.h declares
-EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_combine",
-           "tvmla_status_str", "tvmla_version")
+EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_partials",
+           "tvmla_combine", "tvmla_status_str", "tvmla_version")
 
 
 class TvmlaError(RuntimeError):
@@ -63,6 +63,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_verify.restype = ctypes.c_int
     lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32]
     lib.tvmla_verify_ex.restype = ctypes.c_int
+    lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32]
+    lib.tvmla_verify_partials.restype = ctypes.c_int
     lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
     lib.tvmla_combine.restype = ctypes.c_int
     lib.tvmla_status_str.argtypes = [_I32]
@@ -112,6 +114,20 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _verify_args(q_nope, q_rope, kv_cache, num_draft):
+    ntok, H, dl = q_nope.shape
+    if dl != D_LATENT or tuple(q_rope.shape) != (ntok, H, D_ROPE):
+        raise TvmlaError(2, "q_nope must be [tok, H, 512] and q_rope [tok, H, 64]")
+    if q_nope.stride(2) != 1 or q_rope.stride(2) != 1 or kv_cache.stride(1) != 1:
+        raise TvmlaError(5, "last dimensions must be contiguous")
+    if ntok % num_draft:
+        raise TvmlaError(2, "token count must be batch * num_draft")
+    dt = _dtype_code(q_nope)
+    if q_rope.dtype != q_nope.dtype or kv_cache.dtype != q_nope.dtype:
+        raise TvmlaError(3, "q_nope, q_rope and kv_cache must share one dtype")
+    return ntok // num_draft, H, dt
+
+
 def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
            sm_scale: float, nsplit: int, out, lse, workspace, num_draft: int,
            algo: int = ALGO_AUTO, min_chunk: int = 0, stream=None) -> None:
@@ -120,21 +136,13 @@ def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custo
     q_nope [batch*T, H, 512], q_rope [batch*T, H, 64] (last dim contiguous),
     kv_cache [slots, >=576] (row-contiguous), int32 metadata, uint8 mask,
     out [batch*T, H, 512] (q's dtype), lse [batch*T, H] fp32, workspace a
-    byte tensor of at least workspace_bytes(...) bytes.
+    tensor of at least workspace_bytes(...) bytes.
     """
-    ntok, H, dl = q_nope.shape
-    if dl != D_LATENT or tuple(q_rope.shape) != (ntok, H, D_ROPE):
-        raise TvmlaError(2, "q_nope must be [tok, H, 512] and q_rope [tok, H, 64]")
-    if q_nope.stride(2) != 1 or q_rope.stride(2) != 1 or kv_cache.stride(1) != 1:
-        raise TvmlaError(5, "last dimensions must be contiguous")
-    if ntok % num_draft:
-        raise TvmlaError(2, "token count must be batch * num_draft")
+    batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
     if not (out.is_contiguous() and lse.is_contiguous()):
         raise TvmlaError(5, "out and lse must be contiguous")
-    batch = ntok // num_draft
-    dt = _dtype_code(q_nope)
-    if q_rope.dtype != q_nope.dtype or kv_cache.dtype != q_nope.dtype or out.dtype != q_nope.dtype:
-        raise TvmlaError(3, "q_nope, q_rope, kv_cache and out must share one dtype")
+    if out.dtype != q_nope.dtype:
+        raise TvmlaError(3, "out must have q's dtype")
     st = load().tvmla_verify_ex(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
@@ -142,6 +150,22 @@ def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custo
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         batch, num_draft, H, float(sm_scale), nsplit, dt,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream), algo, min_chunk)
+    _check(st)
+
+
+def verify_partials(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                    sm_scale: float, nsplit: int, workspace, num_draft: int, algo: int = ALGO_AUTO,
+                    min_chunk: int = 0, stream=None) -> None:
+    """Enqueue tvmla_verify_partials: the split step only (partials land in workspace)."""
+    batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
+    st = load().tvmla_verify_partials(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0),
+        _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
+        batch, num_draft, H, float(sm_scale), nsplit, dt,
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_ptr(stream), algo, min_chunk)
     _check(st)
 

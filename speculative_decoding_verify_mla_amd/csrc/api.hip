@@ -50,21 +50,24 @@ const char* tvmla_status_str(int32_t status) {
 
 int32_t tvmla_version(void) { return 100; /* 0.1.0 */ }
 
-tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
-                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
-                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
-                             const int32_t* kv_indices, const int32_t* out_cache_loc,
-                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
-                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
-                             int32_t dtype, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+// Host checks and parameter block shared by tvmla_verify_ex and
+// tvmla_verify_partials. `out`/`lse` are only checked when need_out is set.
+static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                            const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                            const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* out_cache_loc, const uint8_t* custom_mask,
+                            const int32_t* mask_indptr, int32_t batch, int32_t num_draft, int32_t num_heads,
+                            float sm_scale, int32_t nsplit, int32_t dtype, const void* out, const float* lse,
+                            bool need_out, void* workspace, size_t workspace_bytes, int32_t& algo,
+                            int32_t min_chunk, SplitParams& p) {
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
   if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA) return TVMLA_E_ALGO;
   if (algo == TVMLA_ALGO_AUTO) algo = dtype == TVMLA_BF16 ? TVMLA_ALGO_MFMA : TVMLA_ALGO_SCALAR;
   if (algo == TVMLA_ALGO_MFMA && dtype != TVMLA_BF16) return TVMLA_E_DTYPE;
   if (!q_nope || !q_rope || !kv_cache || !kv_indptr || !kv_indices || !out_cache_loc || !custom_mask ||
-      !mask_indptr || !out || !lse)
+      !mask_indptr)
     return TVMLA_E_NULLPTR;
+  if (need_out && (!out || !lse)) return TVMLA_E_NULLPTR;
   if (!workspace) return TVMLA_E_WORKSPACE;
   tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
   if (st != TVMLA_OK) return st;
@@ -73,7 +76,8 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
   if (q_nope_stride_tok < 0 || q_nope_stride_head < 0 || q_rope_stride_tok < 0 || q_rope_stride_head < 0)
     return TVMLA_E_SHAPE;
   const int64_t esz = dtype == TVMLA_BF16 ? 2 : 4;
-  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(out) || !aligned16(workspace))
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(workspace) ||
+      (need_out && !aligned16(out)))
     return TVMLA_E_ALIGN;
   if ((kv_stride_row * esz) % 16 || (q_nope_stride_tok * esz) % 16 || (q_nope_stride_head * esz) % 16 ||
       (q_rope_stride_tok * esz) % 16 || (q_rope_stride_head * esz) % 16)
@@ -81,7 +85,6 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
   const WorkspaceLayout wl = workspace_layout(batch, num_draft, num_heads, nsplit);
   if (workspace_bytes < wl.total) return TVMLA_E_WORKSPACE;
 
-  SplitParams p;
   p.q_nope = q_nope;
   p.qn_stride_tok = q_nope_stride_tok;
   p.qn_stride_head = q_nope_stride_head;
@@ -104,16 +107,31 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
   char* ws = static_cast<char*>(workspace);
   p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
   p.lse_part = reinterpret_cast<float*>(ws + wl.lse_off);
+  return TVMLA_OK;
+}
 
+static hipError_t launch_split(const SplitParams& p, int32_t algo, int32_t dtype, hipStream_t s) {
+  if (algo == TVMLA_ALGO_MFMA) return launch_split_mfma_bf16(p, s);
+  if (dtype == TVMLA_BF16) return launch_split_scalar_bf16(p, s);
+  return launch_split_scalar_fp32(p, s);
+}
+
+tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* out_cache_loc,
+                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                             int32_t dtype, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+  SplitParams p;
+  tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
+                            q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
+                            custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse,
+                            true, workspace, workspace_bytes, algo, min_chunk, p);
+  if (st != TVMLA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (algo == TVMLA_ALGO_MFMA)
-    e = launch_split_mfma_bf16(p, s);
-  else if (dtype == TVMLA_BF16)
-    e = launch_split_scalar_bf16(p, s);
-  else
-    e = launch_split_scalar_fp32(p, s);
-  if (e != hipSuccess) return TVMLA_E_LAUNCH;
+  if (launch_split(p, algo, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
 
   CombineParams c;
   c.o_part = p.o_part;
@@ -127,6 +145,24 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
   c.out = out;
   c.lse = lse;
   if (launch_combine(c, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
+tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                   const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                   const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                   const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                   const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                                   int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                                   int32_t algo, int32_t min_chunk) {
+  SplitParams p;
+  tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
+                            q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
+                            custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, nullptr,
+                            nullptr, false, workspace, workspace_bytes, algo, min_chunk, p);
+  if (st != TVMLA_OK) return st;
+  if (launch_split(p, algo, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
   return TVMLA_OK;
 }
 

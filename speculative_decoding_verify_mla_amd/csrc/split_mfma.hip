@@ -1,20 +1,32 @@
 // bf16 MFMA split kernel for gfx950.
 //
-// Work unit: one workgroup = (request b, split s, group of 128 query rows).
-// A request's rows are r = i*H + h (draft token i, head h); all of them share
-// the request's keys, so one staged key tile feeds up to 128 rows at once --
-// the reuse the sm_120 design reached with 8-head tiles ("The Plan
-// Document", "The Design Reasoning", variant 3), here taken to 128 rows
-// (64 heads x 2 tokens at the usual shape) because the contraction runs on
-// the matrix cores.
+// Work unit: one workgroup = (request b, split s, group of 64 query rows).
+// A request's rows are r = i*H + h (draft token i, head h). Every row of a
+// request attends to the same keys, so one key tile staged in LDS feeds all
+// 64 rows of the group -- the "read the shared latent once, use it for many
+// heads" reuse of "The Plan Document", section "The Design Reasoning"
+// (variants 2 and 3), taken further because the products run on the matrix
+// cores.
 //
-// Per wavefront: 32 query rows. Scores are computed transposed,
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = key tile from LDS, B = the
-// wavefront's 32 query rows, held in registers for the whole split), so the
-// probabilities come out of the MFMA already in the layout the value product
-// O^T += V^T P^T needs as its B operand; V^T (the 512 latent entries of the
-// tile's keys, transposed) is the A operand, read from LDS. The output block
-// O^T (512 x 32 fp32) stays in registers across the split.
+// Tile = 64 keys, staged whole (576 bf16 per key, rows padded to 1168 bytes
+// to skew LDS banks) with direct global->LDS loads (16 bytes per lane, no
+// registers involved), double-buffered: while the four wavefronts work on
+// tile t, tile t+1 is already in flight.
+//
+// Wavefront w = (row block rb = w & 1, key half kh = w >> 1):
+//   scores   S^T = K Q^T for its 32 keys x 32 rows with
+//            v_mfma_f32_32x32x16_bf16 (A = key rows from LDS, B = the row
+//            block's queries, held in registers for the whole split);
+//   softmax  per-row max over the 64-key tile via a 512-byte LDS exchange,
+//            probabilities rounded to bf16 and shared through LDS in the
+//            layout the next MFMA consumes as its B operand;
+//   values   O^T += V^T P^T for latent entries [128w, 128w+128) of BOTH row
+//            blocks, so each V^T operand read from LDS serves 64 rows. V^T is
+//            read straight from the row-major key tile with the gfx950
+//            transpose read (ds_read_b64_tr_b16: within each 16-lane group,
+//            four 64-bit pieces of four rows come back as their columns).
+//   The output block O^T (128 latent entries x 64 rows, fp32) stays in
+//   registers across the split.
 //
 // Schedule and indexing follow page 1, "The Design Emerges": split s of a
 // request with N keys covers [s*chunk, min((s+1)*chunk, N)), chunk =
@@ -23,8 +35,9 @@
 // the mask byte is custom_mask[mask_indptr[b] + i*N + p] (third); P_b comes
 // from kv_indptr (fourth). The online softmax (running max, running sum,
 // rescaled accumulator; page 1, "Input Knowledge Required") rescales the
-// accumulator only when a row's running max grows by more than 2^8, which
-// keeps every probability below 256 and leaves the result unchanged.
+// accumulator only when a row's running max grows by more than 2^8 since the
+// last rescale, which keeps every probability below 256; the normalised
+// result is the same.
 
 #include "tvmla_internal.h"
 
@@ -32,34 +45,66 @@ namespace tvmla {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+#define TVMLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
-constexpr int kWaves = 4;
-constexpr int kRowsWave = 32;
-constexpr int kRowsWG = kWaves * kRowsWave;  // 128 query rows per workgroup
-constexpr int kKT = 32;                       // keys per tile
-constexpr int kKStr = kDKey + 8;              // staged key row: 584 bf16 (1168 B, skews LDS banks)
-constexpr int kVTStr = kKT + 8;               // transposed latent entry: 40 bf16 (80 B)
-constexpr int kQSteps = kDKey / 16;           // 36 k-steps of 16 over the key width
-constexpr int kDBlocks = kDLatent / 32;       // 16 output blocks of 32 latent entries
-constexpr float kRescaleLog2 = 8.f;           // lazy-rescale threshold (log2 units)
+constexpr int kRowsWG = 64;                  // query rows per workgroup (2 blocks of 32)
+constexpr int kKT = 64;                      // keys per tile (2 halves of 32)
+constexpr int kPieces = 73;                  // 16-byte pieces per staged key row (72 + 1 pad)
+constexpr int kRowE = kPieces * 8;           // staged key row stride in bf16 elements
+constexpr int kDmaOps = kKT * kPieces / 64;  // wavefront-wide 16-byte loads per tile
+constexpr int kQSteps = kDKey / 16;          // 36 k-steps of 16 over the key width
+constexpr float kRescaleLog2 = 8.f;          // lazy-rescale threshold (log2 units)
+static_assert(kKT * kPieces % 64 == 0, "tile must be a whole number of wavefront loads");
 
-// Column of tile key k in the transposed latent tile. MFMA output register j
-// of a lane in half `hf` holds key 8*(j/4) + 4*hf + j%4; value-product step c
-// uses registers 8c..8c+7 as its B operand, i.e. keys
-// 16c + 8*(j'/4) + 4*hf + j'%4 for j' = 0..7. Storing key k at column
-// 16c + 8*hf + 4*(j'/4) + j'%4 puts each lane's eight keys side by side.
-__device__ inline int vt_col(int k) {
-  const int c = k >> 4, kp = k & 15;
-  return (c << 4) + (((kp & 7) >> 2) << 3) + ((kp >> 3) << 2) + (kp & 3);
+// Workgroup barrier for LDS exchanges: waits only for this wavefront's LDS
+// operations (lgkmcnt), not for its global loads -- the next tile's
+// direct-to-LDS loads stay in flight across it. (__syncthreads() would add a
+// workgroup fence, i.e. a wait for every outstanding global load.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Barrier at the top of a tile: this wavefront's loads into the tile have
+// landed (vmcnt) and so, after the barrier, have everyone else's.
+// The wait is the compiler builtin (vmcnt(0) expcnt(7) lgkmcnt(0) in the
+// gfx9 encoding) so the compiler knows every earlier load has completed.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ inline uint4 as_u4(bf16x8_t v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
+  typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Enqueue the direct-to-LDS loads of one 64-key tile. LDS piece q*64 + lane
+// (key = piece / 73, column = piece % 73) gets 16 bytes of that key's cache
+// row; the padding column re-reads column 71. slot_reg holds, in lane k, the
+// cache slot of the tile's key k.
+__device__ __forceinline__ void stage_tile(uint16_t* dst, const char* kv, int64_t row_bytes, int slot_reg,
+                                           int wave, int lane) {
+  for (int q = wave; q < kDmaOps; q += 4) {
+    const int pos = q * 64 + lane;
+    const int key = pos / kPieces;
+    int c = pos - key * kPieces;
+    c = c < kPieces - 1 ? c : kPieces - 2;
+    const int slot = __shfl(slot_reg, key, 64);
+    const char* src = kv + (int64_t)slot * row_bytes + c * 16;
+    __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + q * 512), 16, 0, 0);
+  }
+}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(SplitParams p, int groups, int pairs) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKStr];
-  __shared__ __attribute__((aligned(16))) uint16_t VT[kDLatent * kVTStr];
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[kKT * kRowE];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[kKT * kRowE];
+  __shared__ __attribute__((aligned(16))) uint4 pex[4 * 2 * 64];  // P^T operands: [wave][k-step][lane]
+  __shared__ float mex[4 * 32];                                   // per-wavefront row maxima / sums
 
   // Workgroup ids reach the 8 XCDs round-robin (id % 8). Every row group of
   // one (request, split) pair gets the same id % 8, so the pair's key rows
@@ -82,21 +127,23 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
   if (start >= end) return;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hf = lane >> 5;   // which 8-wide half of each 16-wide k-step this lane feeds
-  const int col = lane & 31;  // MFMA column = this lane's query row within the wavefront
-  const int r = g * kRowsWG + wave * kRowsWave + col;
-  const bool row_ok = r < R;
-  // A row past the end computes on row R-1's data (its column of each MFMA
-  // is independent of the others) and is never written.
-  const int rr = row_ok ? r : R - 1;
+  const int col = lane & 31;  // MFMA column = query row within the row block
+  const int rb = wave & 1;    // row block whose scores this wavefront computes
+  const int kh = wave >> 1;   // key half of each tile it scores
+  const int64_t tb = (int64_t)b * p.num_draft;  // first draft token of request b
+
+  // This lane's scoring row. A row past the end computes on row R-1's data
+  // (each MFMA column is independent) and is never written.
+  const int r = g * kRowsWG + rb * 32 + col;
+  const int rr = r < R ? r : R - 1;
   const int i = rr / p.num_heads;
   const int h = rr - i * p.num_heads;
-  const int64_t tb = (int64_t)b * p.num_draft;  // first draft token of request b
   const int64_t t = tb + i;
 
-  // Q^T fragments: query row `col`, key entries [16ks + 8hf, 16ks + 8hf + 8).
+  // Q^T operands: query row `col` of block rb, key entries [16ks + 8hf, +8).
   bf16x8_t qf[kQSteps];
   {
     const uint16_t* qn = static_cast<const uint16_t*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head + 8 * hf;
@@ -108,131 +155,202 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
       qf[kDLatent / 16 + ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * ks));
   }
 
-  f32x16_t o[kDBlocks];
+  f32x16_t o[2][4];  // O^T blocks: [row block][32-entry block of this wavefront's 128 entries]
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-  float m_ref = -INFINITY;  // reference max (log2 units) the accumulator is scaled to
-  float l_part = 0.f;       // this lane's share of the softmax sum
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[x][db][j] = 0.f;
+  float m_ref[2] = {-INFINITY, -INFINITY};  // per row block: reference max (log2 units)
+  float l_part = 0.f;                       // this lane's share of its scoring row's softmax sum
 
   const float scale2 = p.sm_scale * kLog2e;
-  const uint8_t* mrow = p.mask + p.mask_indptr[b] + (int64_t)i * N;
-  const uint16_t* kv = static_cast<const uint16_t*>(p.kv);
+  const char* kvb = static_cast<const char*>(p.kv);
+  const int64_t row_bytes = p.kv_stride * 2;
 
-  for (int p0 = start; p0 < end; p0 += kKT) {
-    __syncthreads();  // every wavefront is done with the previous tile
+  // Slot of key `key` of this request (keys past the split's end re-read the
+  // last key: finite data whose probability is forced to zero).
+  auto slot_of = [&](int key) -> int {
+    key = key < end ? key : end - 1;
+    return key < P ? p.kv_indices[ip0 + key] : p.out_cache_loc[tb + (key - P)];
+  };
+  // Visibility. The 32 rows of this wavefront's block belong to draft tokens
+  // tok0 .. tok0+ntok-1 (one token when H is a multiple of 32). For each such
+  // token, lane k (both halves alike) reads the mask byte of tile key
+  // 32kh + k, and one ballot turns the 32 bytes into a bit mask; each lane
+  // keeps its own token's. Bytes for up to eight tokens are prefetched one
+  // tile ahead; blocks spanning more tokens (fewer than five heads) read the
+  // rest when needed.
+  const int rfirst = min(g * kRowsWG + rb * 32, R - 1);
+  const int rlast = min(g * kRowsWG + rb * 32 + 31, R - 1);
+  const int tok0 = rfirst / p.num_heads;
+  const int ntok = rlast / p.num_heads - tok0 + 1;
+  const int my_u = i - tok0;
+  const uint8_t* mbase = p.mask + p.mask_indptr[b] + (int64_t)tok0 * N;
+  uint8_t mnext[8];
+  auto load_mask = [&](int p0) {
+    int key = p0 + 32 * kh + col;
+    key = key < end ? key : end - 1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < ntok) mnext[u] = mbase[(int64_t)u * N + key];
+  };
+  auto visible_bits = [&](int p0) -> uint32_t {  // bit k: tile key 32kh + k visible to my row
+    const int key = p0 + 32 * kh + col;
+    const bool kok = key < end;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < ntok) {
+        const uint32_t bal = (uint32_t)__ballot(kok && mnext[u] != 0);
+        mine = u == my_u ? bal : mine;
+      }
+    for (int u = 8; u < ntok; ++u) {
+      const uint32_t bal = (uint32_t)__ballot(kok && mbase[(int64_t)u * N + (kok ? key : end - 1)] != 0);
+      mine = u == my_u ? bal : mine;
+    }
+    return mine;
+  };
 
-    // ---- stage the tile: lane -> key `col`, 16-byte pieces 2*(wave + 4q) + hf
-    {
-      // A key past the split's end re-reads the last key's row: finite data
-      // whose probability is forced to zero below.
-      const int key = min(p0 + col, end - 1);
-      const int slot = key < P ? p.kv_indices[ip0 + key] : p.out_cache_loc[tb + (key - P)];
-      const uint16_t* src = kv + (int64_t)slot * p.kv_stride;
-      uint4 v[9];
+  const int ntiles = (end - start + kKT - 1) / kKT;
+  int slot_reg = slot_of(start + lane);
+  stage_tile(kb0, kvb, row_bytes, slot_reg, wave, lane);
+  load_mask(start);
+  if (ntiles > 1) slot_reg = slot_of(start + kKT + lane);
+
+  auto rescale = [&](int x, float tmax) {
+    const float m_new = fmaxf(m_ref[x], tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref[x] - m_new);
 #pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        const int piece = 2 * (wave + 4 * q) + hf;
-        v[q] = *reinterpret_cast<const uint4*>(src + 8 * piece);
-      }
-      const int vc = vt_col(col);
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        const int piece = 2 * (wave + 4 * q) + hf;
-        *reinterpret_cast<uint4*>(&Ks[col * kKStr + 8 * piece]) = v[q];
-        if (piece < kDLatent / 8) {
-          const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            VT[(8 * piece + 2 * e) * kVTStr + vc] = (uint16_t)(w4[e] & 0xffffu);
-            VT[(8 * piece + 2 * e + 1) * kVTStr + vc] = (uint16_t)(w4[e] >> 16);
-          }
-        }
-      }
+      for (int j = 0; j < 16; ++j) o[x][db][j] *= alpha;
+    if (x == rb) l_part *= alpha;
+    m_ref[x] = m_new;
+  };
+
+  auto body = [&](int tile, const uint16_t* cur, uint16_t* nxt) {
+    const int p0 = start + tile * kKT;
+    tile_barrier();  // tile in LDS; every wavefront is done with the previous one
+    // score register j of lane half hf holds tile key 32kh + 8(j/4) + 4hf + j%4
+    const uint32_t vis = visible_bits(p0) >> (4 * hf);
+    if (tile + 1 < ntiles) {
+      stage_tile(nxt, kvb, row_bytes, slot_reg, wave, lane);
+      load_mask(p0 + kKT);
+      if (tile + 2 < ntiles) slot_reg = slot_of(p0 + 2 * kKT + lane);
     }
 
-    // ---- visibility of this lane's 16 keys: 8*(j/4) + 4*hf + j%4
-    uint32_t vis = 0;
+    // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb
+    const uint16_t* kbase = cur + (32 * kh + col) * kRowE + 8 * hf;
+    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16_t sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(kbase), qf[0], zero,
+                                                            0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = p0 + 8 * (j >> 2) + 4 * hf + (j & 3);
-      const bool v = key < end && mrow[key] != 0;
-      vis |= (uint32_t)v << j;
-    }
-    __syncthreads();  // the tile is in LDS
-
-    // ---- S^T = K Q^T (32 keys x 32 rows), fp32 accumulation
-    f32x16_t sacc;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-    const uint16_t* kbase = Ks + col * kKStr + 8 * hf;
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
+    for (int ks = 1; ks < kQSteps; ++ks) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * ks);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
     }
 
-    // ---- online softmax for row `col` (the two halves hold 16 keys each)
+    // ---- row maxima over the whole 64-key tile (two wavefronts per row block)
     float sv[16];
-    float tmax = -INFINITY;
+    float tm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      sv[j] = ((vis >> j) & 1u) ? sacc[j] * scale2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[j]);
+      sv[j] = ((vis >> (8 * (j >> 2) + (j & 3))) & 1u) ? sacc[j] * scale2 : -INFINITY;
+      tm = fmaxf(tm, sv[j]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (__ballot(tmax > m_ref + kRescaleLog2)) {
-      const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-      m_ref = m_new;
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    if (hf == 0) mex[wave * 32 + col] = tm;
+    lds_barrier();
+    const float tm0 = fmaxf(mex[col], mex[64 + col]);       // row block 0: wavefronts 0, 2
+    const float tm1 = fmaxf(mex[32 + col], mex[96 + col]);  // row block 1: wavefronts 1, 3
+    // Every wavefront sees the same maxima and the same m_ref, so all four
+    // take the same decision and keep identical references.
+    if (__ballot(tm0 > m_ref[0] + kRescaleLog2 || tm1 > m_ref[1] + kRescaleLog2)) {
+      rescale(0, tm0);
+      rescale(1, tm1);
     }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
+    // ---- probabilities of this wavefront's 32 keys x 32 rows
+    float mu = rb == 0 ? m_ref[0] : m_ref[1];
+    mu = mu == -INFINITY ? 0.f : mu;
     bf16x8_t pf[2];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pj = exp2f(sv[j] - m_use);
+      const float pj = exp2f(sv[j] - mu);
       psum += pj;
       pf[j >> 3][j & 7] = (__bf16)pj;
     }
     l_part += psum;
+    pex[(wave * 2 + 0) * 64 + lane] = as_u4(pf[0]);
+    pex[(wave * 2 + 1) * 64 + lane] = as_u4(pf[1]);
+    lds_barrier();
 
-    // ---- O^T += V^T P^T over the 512 latent entries
+    // ---- O^T += V^T P^T for latent entries [128 wave, +128), both row blocks.
+    // Output register j of the score MFMA in lane half hf holds key
+    // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
+    // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
+    // The transposed reads fetch V rows base..base+3 and base+8..base+11.
+    const int vkey = 4 * hf + ((lane & 15) >> 2);
+    const int vdim = 128 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
-      const uint16_t* vrow = VT + (32 * db + col) * kVTStr + 8 * hf;
+    for (int kh2 = 0; kh2 < 2; ++kh2) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vrow + 16 * c);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], o[db], 0, 0, 0);
+        const uint16_t* vb = cur + (32 * kh2 + 16 * c + vkey) * kRowE + vdim;
+        bf16x8_t va[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + 32 * db));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + 8 * kRowE + 32 * db));
+          va[db] = cat4(lo, hi);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const bf16x8_t pb = as_bf16x8(pex[((x + 2 * kh2) * 2 + c) * 64 + lane]);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            o[x][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb, o[x][db], 0, 0, 0);
+        }
       }
     }
+  };
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const bool odd = tile & 1;
+    body(tile, odd ? kb1 : kb0, odd ? kb0 : kb1);
   }
 
-  // ---- partial result: o / l and lse for this split
-  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
-  if (row_ok) {
-    const size_t prow = ((size_t)b * p.nsplit + s) * R + r;
-    float* dst = p.o_part + prow * kDLatent + 4 * hf;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // ---- row sums: two wavefronts x two lane halves per row
+  const float lt = l_part + __shfl_xor(l_part, 32, 64);
+  lds_barrier();
+  if (hf == 0) mex[wave * 32 + col] = lt;
+  lds_barrier();
+  const float lrow[2] = {mex[col] + mex[64 + col], mex[32 + col] + mex[96 + col]};
+
+  // ---- partial results: entries [128 wave, +128) of both row blocks
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
+  for (int x = 0; x < 2; ++x) {
+    const int row = g * kRowsWG + 32 * x + col;
+    if (row >= R) continue;
+    const size_t prow = ((size_t)b * p.nsplit + s) * R + row;
+    float* dst = p.o_part + prow * kDLatent + 128 * wave + 4 * hf;
+    const float inv = lrow[x] > 0.f ? 1.f / lrow[x] : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         float4 v;
-        v.x = o[db][4 * jg + 0] * inv;
-        v.y = o[db][4 * jg + 1] * inv;
-        v.z = o[db][4 * jg + 2] * inv;
-        v.w = o[db][4 * jg + 3] * inv;
+        v.x = o[x][db][4 * jg + 0] * inv;
+        v.y = o[x][db][4 * jg + 1] * inv;
+        v.z = o[x][db][4 * jg + 2] * inv;
+        v.w = o[x][db][4 * jg + 3] * inv;
         *reinterpret_cast<float4*>(dst + 32 * db + 8 * jg) = v;
       }
-    if (hf == 0) p.lse_part[prow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (wave == 0 && hf == 0)
+      p.lse_part[prow] = lrow[x] > 0.f ? (m_ref[x] + log2f(lrow[x])) * kLn2 : -INFINITY;
   }
 }
 

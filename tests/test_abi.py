@@ -135,3 +135,15 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(FileNotFoundError):
         binding.load(str(tmp_path / "missing.so"))
+
+
+def test_partials_errors(lib):
+    f = lib.tvmla_verify_partials
+    ws = binding.workspace_bytes(1, 4, 64, 64)
+    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 4, 64, 0.07,
+            64, binding.BF16, _FAKE, ws, None, 0, 0]
+    for idx, val, code in [(0, None, 1), (6, None, 1), (19, None, 4), (20, ws - 1, 4), (13, 0, 2), (18, 7, 3),
+                           (22, 9, 7), (7, 580, 5), (23, -1, 2)]:
+        a = list(good)
+        a[idx] = val
+        assert f(*a) == code, (idx, val)

@@ -296,3 +296,20 @@ def test_graph_capture_replay():
             compare(x, go, gl, ro, rl, f"replay{rep}/P={list(x.prefix_lens)}")
             eo, el = d.result()  # eager, same buffers
             assert np.array_equal(go, eo) and np.array_equal(gl, el)
+
+
+def test_partials_then_combine_equals_verify():
+    w = gen.build(SMALL["groups_h64"])
+    d = Device(w)
+    for algo in (MFMA, SCALAR):
+        o1, l1 = d.result(algo=algo)
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.ws.fill_(float("nan"))
+        binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
+                                d.custom_mask, d.mask_indptr, w.sm_scale, d.nsplit, d.ws, w.num_draft, algo=algo)
+        binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, d.nsplit, d.out, d.lse)
+        torch.cuda.synchronize()
+        o2 = d.out.float().cpu().numpy().astype(np.float64)
+        l2 = d.lse.cpu().numpy().astype(np.float64)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
