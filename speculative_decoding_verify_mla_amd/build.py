@@ -22,6 +22,12 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "split_scalar.hip", "split_mfma.hip", "combine.hip"]
 
+# Per-file flags. The MFMA split kernel keeps its accumulators in VGPRs
+# (MFMA destination/accumulator in the VGPR file) so the online-softmax
+# rescale is plain vector arithmetic; the query operands then sit in AGPRs,
+# which the MFMA reads directly.
+FILE_FLAGS = {"split_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # Packed fp32 VALU ops are disabled on purpose (-packed-fp32-ops): the
 # compiler would otherwise form v_pk_* fp32 instructions from float code.
 CFLAGS = [
@@ -58,7 +64,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        flags = [*CFLAGS, *FILE_FLAGS.get(src, []), *extra]
+        out = _run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj, out
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:

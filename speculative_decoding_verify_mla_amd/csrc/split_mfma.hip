@@ -8,10 +8,13 @@
 // (variants 2 and 3), taken further because the products run on the matrix
 // cores.
 //
-// Tile = 64 keys, staged whole (576 bf16 per key, rows padded to 1168 bytes
-// to skew LDS banks) with direct global->LDS loads (16 bytes per lane, no
-// registers involved), double-buffered: while the four wavefronts work on
-// tile t, tile t+1 is already in flight.
+// Tile = 64 keys, staged whole with direct global->LDS loads (16 bytes per
+// lane, no registers involved), double-buffered: while the four wavefronts
+// work on tile t, tile t+1 is already in flight. In LDS a tile is a latent
+// region (64 keys x 1024 bytes; one wavefront-wide load per key) followed by
+// a rope region (64 keys x 128 bytes; one load per 8 keys). Within a key's
+// row the 16-byte pieces are XOR-swizzled by a function of the key, so the
+// MFMA operand reads of consecutive keys hit different LDS banks.
 //
 // Wavefront w = (row block rb = w & 1, key half kh = w >> 1):
 //   scores   S^T = K Q^T for its 32 keys x 32 rows with
@@ -49,14 +52,21 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 #define TVMLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
-constexpr int kRowsWG = 64;                  // query rows per workgroup (2 blocks of 32)
-constexpr int kKT = 64;                      // keys per tile (2 halves of 32)
-constexpr int kPieces = 73;                  // 16-byte pieces per staged key row (72 + 1 pad)
-constexpr int kRowE = kPieces * 8;           // staged key row stride in bf16 elements
-constexpr int kDmaOps = kKT * kPieces / 64;  // wavefront-wide 16-byte loads per tile
-constexpr int kQSteps = kDKey / 16;          // 36 k-steps of 16 over the key width
-constexpr float kRescaleLog2 = 8.f;          // lazy-rescale threshold (log2 units)
-static_assert(kKT * kPieces % 64 == 0, "tile must be a whole number of wavefront loads");
+constexpr int kRowsWG = 64;   // query rows per workgroup (2 blocks of 32)
+constexpr int kKT = 64;       // keys per tile (2 halves of 32)
+constexpr int kLatRow = 1024; // bytes of one key's latent part in LDS (64 pieces of 16 B)
+constexpr int kRopeRow = 128; // bytes of one key's rope part in LDS (8 pieces)
+constexpr int kTileLat = kKT * kLatRow;
+constexpr int kTileBytes = kTileLat + kKT * kRopeRow;  // 73,728 bytes per tile buffer
+constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
+constexpr float kRescaleLog2 = 8.f;                    // lazy-rescale threshold (log2 units)
+
+// Piece swizzle of key k: a permutation of 0..15 over 16 consecutive keys
+// (the 16 lanes an LDS read cycle serves for the score operand) whose bits
+// 1..3 also differ across 4 consecutive keys (the 4 rows a transposed read
+// of 16 lanes covers, two adjacent pieces each). Latent pieces XOR all four
+// bits (staying inside their aligned group of 16), rope pieces the low three.
+__device__ __forceinline__ int piece_swz(int k) { return ((k >> 2) & 1) | ((k & 3) << 1) | (k & 8); }
 
 // Workgroup barrier for LDS exchanges: waits only for this wavefront's LDS
 // operations (lgkmcnt), not for its global loads -- the next tile's
@@ -82,27 +92,41 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Enqueue the direct-to-LDS loads of one 64-key tile. LDS piece q*64 + lane
-// (key = piece / 73, column = piece % 73) gets 16 bytes of that key's cache
-// row; the padding column re-reads column 71. slot_reg holds, in lane k, the
-// cache slot of the tile's key k.
-__device__ __forceinline__ void stage_tile(uint16_t* dst, const char* kv, int64_t row_bytes, int slot_reg,
-                                           int wave, int lane) {
-  for (int q = wave; q < kDmaOps; q += 4) {
-    const int pos = q * 64 + lane;
-    const int key = pos / kPieces;
-    int c = pos - key * kPieces;
-    c = c < kPieces - 1 ? c : kPieces - 2;
-    const int slot = __shfl(slot_reg, key, 64);
-    const char* src = kv + (int64_t)slot * row_bytes + c * 16;
-    __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + q * 512), 16, 0, 0);
+// Enqueue the direct-to-LDS loads of one 64-key tile into `dst`. slot_reg
+// holds, in lane k, the cache slot of the tile's key k.
+//   latent: key k = wave + 4u; a buffer resource over the key's cache row
+//           (scalar registers only; its 1152-byte size also bounds the read)
+//           and lane l loads piece l ^ swz(k) into LDS piece l of the key's
+//           1024-byte latent row;
+//   rope:   keys 8v..8v+7 (v = wave + 4u); lane l serves key 8v + l/8 and
+//           loads rope piece (l%8) ^ (swz & 7) into LDS piece l%8 of its row.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
+
+__device__ __forceinline__ void stage_tile(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int u = 0; u < kKT / 4; ++u) {
+    const int k = wave + 4 * u;
+    const int slot = __builtin_amdgcn_readlane(slot_reg, k);
+    const __amdgpu_buffer_rsrc_t row =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kv + (int64_t)slot * row_bytes), 0, kDKey * 2, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(row, TVMLA_LDS(void, dst + k * kLatRow), 16,
+                                             (lane ^ piece_swz(k)) << 4, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kKT / 32; ++u) {
+    const int v = wave + 4 * u;
+    const int k = 8 * v + (lane >> 3);
+    const int slot = __shfl(slot_reg, k, 64);
+    const char* src = kv + (int64_t)slot * row_bytes + kDLatent * 2 + (((lane & 7) ^ (piece_swz(k) & 7)) << 4);
+    __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
   }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(SplitParams p, int groups, int pairs) {
-  __shared__ __attribute__((aligned(16))) uint16_t kb0[kKT * kRowE];
-  __shared__ __attribute__((aligned(16))) uint16_t kb1[kKT * kRowE];
+  __shared__ __attribute__((aligned(16))) char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char kb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint4 pex[4 * 2 * 64];  // P^T operands: [wave][k-step][lane]
   __shared__ float mex[4 * 32];                                   // per-wavefront row maxima / sums
 
@@ -164,6 +188,33 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
       for (int j = 0; j < 16; ++j) o[x][db][j] = 0.f;
   float m_ref[2] = {-INFINITY, -INFINITY};  // per row block: reference max (log2 units)
   float l_part = 0.f;                       // this lane's share of its scoring row's softmax sum
+
+  // Per-lane LDS byte offsets inside a tile buffer.
+  //   score operand (A of S^T = K Q^T): key qkey = 32kh + col, k-step ks
+  //   reads latent piece 2ks + hf at (2ks + hf) ^ swz(qkey); the XOR touches the low
+  //   four bits only, so the offset is 256 (ks / 8) + qoff[ks % 8]; rope
+  //   k-step 32 + b reads rope piece (2b + hf) ^ (swz(qkey) & 7).
+  const int qkey = 32 * kh + col;
+  const int sq = piece_swz(qkey);
+  int qoff[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) qoff[x] = qkey * kLatRow + (((2 * x + hf) ^ sq) << 4);
+  int roff[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) roff[x] = kTileLat + qkey * kRopeRow + (((2 * x + hf) ^ (sq & 7)) << 4);
+  //   value operand (A of O^T += V^T P^T, transposed reads): lane group row
+  //   vr = (lane & 15) / 4 reads keys 32kh2 + 16c + 4hf + vr (+8), latent
+  //   entries d = 128w + 32db + 16g1 + 4(lane & 3) .. +3 (g1 = lane bit 4),
+  //   i.e. piece 16w + 4db + 2g1 + (lane & 3) / 2, byte 8 (lane & 1).
+  const int vr = 4 * hf + ((lane & 15) >> 2);
+  const int vpl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int voff[2][4];  // [+8 keys][db]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      voff[x][db] = (vr + 8 * x) * kLatRow + ((16 * wave + ((4 * db + vpl) ^ piece_swz(vr + 8 * x))) << 4) +
+                    8 * (lane & 1);
 
   const float scale2 = p.sm_scale * kLog2e;
   const char* kvb = static_cast<const char*>(p.kv);
@@ -230,7 +281,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     m_ref[x] = m_new;
   };
 
-  auto body = [&](int tile, const uint16_t* cur, uint16_t* nxt) {
+  auto body = [&](int tile, const char* cur, char* nxt) {
     const int p0 = start + tile * kKT;
     tile_barrier();  // tile in LDS; every wavefront is done with the previous one
     // score register j of lane half hf holds tile key 32kh + 8(j/4) + 4hf + j%4
@@ -242,14 +293,27 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     }
 
     // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb
-    const uint16_t* kbase = cur + (32 * kh + col) * kRowE + 8 * hf;
-    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    f32x16_t sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(kbase), qf[0], zero,
-                                                            0, 0, 0);
+    // The four k-steps ahead are read into a ring of operand registers so
+    // each MFMA's LDS read was issued four MFMAs earlier.
+    auto kfrag = [&](int ks) -> bf16x8_t {
+      const int off = ks < 32 ? qoff[ks & 7] + 256 * (ks >> 3) : roff[ks - 32];
+      return *reinterpret_cast<const bf16x8_t*>(cur + off);
+    };
+    bf16x8_t ring[4];
 #pragma unroll
-    for (int ks = 1; ks < kQSteps; ++ks) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * ks);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
+    for (int x = 0; x < 4; ++x) ring[x] = kfrag(x);
+    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16_t sacc = zero;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks & 3], qf[ks], sacc, 0, 0, 0);
+      if (ks + 4 < kQSteps) ring[ks & 3] = kfrag(ks + 4);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first four operand reads
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA ...
+      if (ks + 4 < kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // ... then the read 4 ahead
     }
 
     // ---- row maxima over the whole 64-key tile (two wavefronts per row block)
@@ -293,18 +357,16 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
     // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
     // The transposed reads fetch V rows base..base+3 and base+8..base+11.
-    const int vkey = 4 * hf + ((lane & 15) >> 2);
-    const int vdim = 128 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int kh2 = 0; kh2 < 2; ++kh2) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint16_t* vb = cur + (32 * kh2 + 16 * c + vkey) * kRowE + vdim;
+        const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow;
         bf16x8_t va[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + 32 * db));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + 8 * kRowE + 32 * db));
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + voff[0][db]));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + voff[1][db]));
           va[db] = cat4(lo, hi);
         }
 #pragma unroll
