@@ -83,6 +83,9 @@ def main(argv=None):
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the verify step, time a plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM traffic counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -100,6 +103,22 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = "cuda"
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_bytes": n, "ms": ms, "read_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+        return 0
     w = gen.build(args.workload)
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
     pool = w.device_pool(dev, fill=0.0)

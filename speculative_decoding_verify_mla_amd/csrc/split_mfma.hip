@@ -83,6 +83,25 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16) issued through inline asm. The
+// compiler treats the builtin as touching any LDS location and would wait
+// for every in-flight direct-to-LDS load before it; here the caller waits
+// for the result explicitly with lds_wait8 before using it.
+__device__ __forceinline__ i16x4_t tr_read(const char* lds_ptr) {
+  const uint32_t a = (uint32_t)(uintptr_t)TVMLA_LDS(const char, lds_ptr);
+  i16x4_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+
+// Wait for all outstanding LDS reads; the eight registers are tied to the
+// wait so no use of them can be scheduled before it.
+__device__ __forceinline__ void lds_wait8(i16x4_t& a0, i16x4_t& a1, i16x4_t& a2, i16x4_t& a3, i16x4_t& b0,
+                                          i16x4_t& b1, i16x4_t& b2, i16x4_t& b3) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+}
+
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ inline uint4 as_u4(bf16x8_t v) { return __builtin_bit_cast(uint4, v); }
 
@@ -92,8 +111,9 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Enqueue the direct-to-LDS loads of one 64-key tile into `dst`. slot_reg
-// holds, in lane k, the cache slot of the tile's key k.
+// Direct-to-LDS loads of one 64-key tile into `dst` (issued in five pieces
+// spread over the previous tile's compute). slot_reg holds, in lane k, the
+// cache slot of the tile's key k.
 //   latent: key k = wave + 4u; a buffer resource over the key's cache row
 //           (scalar registers only; its 1152-byte size also bounds the read)
 //           and lane l loads piece l ^ swz(k) into LDS piece l of the key's
@@ -102,10 +122,11 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 //           loads rope piece (l%8) ^ (swz & 7) into LDS piece l%8 of its row.
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
 
-__device__ __forceinline__ void stage_tile(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
-                                           int lane) {
+// Latent loads for keys k = wave + 4u, u in [4 part, 4 part + 4).
+__device__ __forceinline__ void stage_latent(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
+                                             int lane, int part) {
 #pragma unroll
-  for (int u = 0; u < kKT / 4; ++u) {
+  for (int u = 4 * part; u < 4 * part + 4; ++u) {
     const int k = wave + 4 * u;
     const int slot = __builtin_amdgcn_readlane(slot_reg, k);
     const __amdgpu_buffer_rsrc_t row =
@@ -113,6 +134,11 @@ __device__ __forceinline__ void stage_tile(char* dst, const char* kv, int64_t ro
     __builtin_amdgcn_raw_ptr_buffer_load_lds(row, TVMLA_LDS(void, dst + k * kLatRow), 16,
                                              (lane ^ piece_swz(k)) << 4, 0, 0, 0);
   }
+}
+
+// Rope loads: keys 8v..8v+7, v = wave + 4u.
+__device__ __forceinline__ void stage_rope(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
+                                           int lane) {
 #pragma unroll
   for (int u = 0; u < kKT / 32; ++u) {
     const int v = wave + 4 * u;
@@ -186,7 +212,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[x][db][j] = 0.f;
-  float m_ref[2] = {-INFINITY, -INFINITY};  // per row block: reference max (log2 units)
+  float m_ref0 = -INFINITY, m_ref1 = -INFINITY;  // per row block: reference max (log2 units)
   float l_part = 0.f;                       // this lane's share of its scoring row's softmax sum
 
   // Per-lane LDS byte offsets inside a tile buffer.
@@ -220,44 +246,44 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   const char* kvb = static_cast<const char*>(p.kv);
   const int64_t row_bytes = p.kv_stride * 2;
 
-  // Slot of key `key` of this request (keys past the split's end re-read the
-  // last key: finite data whose probability is forced to zero).
+  // Slot of key `key` of this request. Keys past the split's end re-read the
+  // last key (finite data whose probability is forced to zero), so every
+  // load below is in bounds without a branch.
   auto slot_of = [&](int key) -> int {
     key = key < end ? key : end - 1;
-    return key < P ? p.kv_indices[ip0 + key] : p.out_cache_loc[tb + (key - P)];
+    const int32_t* src = key < P ? p.kv_indices + ip0 + key : p.out_cache_loc + tb + (key - P);
+    return *src;
   };
   // Visibility. The 32 rows of this wavefront's block belong to draft tokens
   // tok0 .. tok0+ntok-1 (one token when H is a multiple of 32). For each such
   // token, lane k (both halves alike) reads the mask byte of tile key
   // 32kh + k, and one ballot turns the 32 bytes into a bit mask; each lane
-  // keeps its own token's. Bytes for up to eight tokens are prefetched one
-  // tile ahead; blocks spanning more tokens (fewer than five heads) read the
-  // rest when needed.
+  // keeps its own token's. Bytes for four tokens are prefetched one tile
+  // ahead (token indices clamped to the block's last); blocks spanning more
+  // tokens (fewer than eight heads) read the rest when needed.
   const int rfirst = min(g * kRowsWG + rb * 32, R - 1);
   const int rlast = min(g * kRowsWG + rb * 32 + 31, R - 1);
   const int tok0 = rfirst / p.num_heads;
   const int ntok = rlast / p.num_heads - tok0 + 1;
   const int my_u = i - tok0;
   const uint8_t* mbase = p.mask + p.mask_indptr[b] + (int64_t)tok0 * N;
-  uint8_t mnext[8];
+  uint8_t mnext[4];
   auto load_mask = [&](int p0) {
     int key = p0 + 32 * kh + col;
     key = key < end ? key : end - 1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < ntok) mnext[u] = mbase[(int64_t)u * N + key];
+    for (int u = 0; u < 4; ++u) mnext[u] = mbase[(int64_t)min(u, ntok - 1) * N + key];
   };
   auto visible_bits = [&](int p0) -> uint32_t {  // bit k: tile key 32kh + k visible to my row
     const int key = p0 + 32 * kh + col;
     const bool kok = key < end;
     uint32_t mine = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < ntok) {
-        const uint32_t bal = (uint32_t)__ballot(kok && mnext[u] != 0);
-        mine = u == my_u ? bal : mine;
-      }
-    for (int u = 8; u < ntok; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t bal = (uint32_t)__ballot(kok && mnext[u] != 0);
+      mine = u == my_u ? bal : mine;
+    }
+    for (int u = 4; u < ntok; ++u) {
       const uint32_t bal = (uint32_t)__ballot(kok && mbase[(int64_t)u * N + (kok ? key : end - 1)] != 0);
       mine = u == my_u ? bal : mine;
     }
@@ -266,19 +292,21 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
 
   const int ntiles = (end - start + kKT - 1) / kKT;
   int slot_reg = slot_of(start + lane);
-  stage_tile(kb0, kvb, row_bytes, slot_reg, wave, lane);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) stage_latent(kb0, kvb, row_bytes, slot_reg, wave, lane, part);
+  stage_rope(kb0, kvb, row_bytes, slot_reg, wave, lane);
   load_mask(start);
-  if (ntiles > 1) slot_reg = slot_of(start + kKT + lane);
+  slot_reg = slot_of(start + kKT + lane);
 
-  auto rescale = [&](int x, float tmax) {
-    const float m_new = fmaxf(m_ref[x], tmax);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref[x] - m_new);
+  auto rescale = [&](f32x16_t (&ox)[4], float& mref, bool mine, float tmax) {
+    const float m_new = fmaxf(mref, tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - m_new);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[x][db][j] *= alpha;
-    if (x == rb) l_part *= alpha;
-    m_ref[x] = m_new;
+      for (int j = 0; j < 16; ++j) ox[db][j] *= alpha;
+    if (mine) l_part *= alpha;
+    mref = m_new;
   };
 
   auto body = [&](int tile, const char* cur, char* nxt) {
@@ -286,15 +314,16 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     tile_barrier();  // tile in LDS; every wavefront is done with the previous one
     // score register j of lane half hf holds tile key 32kh + 8(j/4) + 4hf + j%4
     const uint32_t vis = visible_bits(p0) >> (4 * hf);
-    if (tile + 1 < ntiles) {
-      stage_tile(nxt, kvb, row_bytes, slot_reg, wave, lane);
-      load_mask(p0 + kKT);
-      if (tile + 2 < ntiles) slot_reg = slot_of(p0 + 2 * kKT + lane);
-    }
+    // Prefetch for the next tiles. On the last tile these re-read clamped,
+    // valid rows into the idle buffer; nothing reads them.
+    load_mask(p0 + kKT);
+    const int slot_cur = slot_reg;
+    slot_reg = slot_of(p0 + 2 * kKT + lane);
 
-    // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb
+    // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb.
     // The four k-steps ahead are read into a ring of operand registers so
-    // each MFMA's LDS read was issued four MFMAs earlier.
+    // each MFMA's LDS read was issued four MFMAs earlier; the next tile's
+    // loads are issued in three groups of four keys between the MFMAs.
     auto kfrag = [&](int ks) -> bf16x8_t {
       const int off = ks < 32 ? qoff[ks & 7] + 256 * (ks >> 3) : roff[ks - 32];
       return *reinterpret_cast<const bf16x8_t*>(cur + off);
@@ -306,14 +335,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     f32x16_t sacc = zero;
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
+      if (ks % 12 == 0) stage_latent(nxt, kvb, row_bytes, slot_cur, wave, lane, ks / 12);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks & 3], qf[ks], sacc, 0, 0, 0);
       if (ks + 4 < kQSteps) ring[ks & 3] = kfrag(ks + 4);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first four operand reads
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA ...
-      if (ks + 4 < kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // ... then the read 4 ahead
     }
 
     // ---- row maxima over the whole 64-key tile (two wavefronts per row block)
@@ -331,19 +355,19 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     const float tm1 = fmaxf(mex[32 + col], mex[96 + col]);  // row block 1: wavefronts 1, 3
     // Every wavefront sees the same maxima and the same m_ref, so all four
     // take the same decision and keep identical references.
-    if (__ballot(tm0 > m_ref[0] + kRescaleLog2 || tm1 > m_ref[1] + kRescaleLog2)) {
-      rescale(0, tm0);
-      rescale(1, tm1);
+    if (__ballot(tm0 > m_ref0 + kRescaleLog2 || tm1 > m_ref1 + kRescaleLog2)) {
+      rescale(o[0], m_ref0, rb == 0, tm0);
+      rescale(o[1], m_ref1, rb == 1, tm1);
     }
 
     // ---- probabilities of this wavefront's 32 keys x 32 rows
-    float mu = rb == 0 ? m_ref[0] : m_ref[1];
+    float mu = rb == 0 ? m_ref0 : m_ref1;
     mu = mu == -INFINITY ? 0.f : mu;
     bf16x8_t pf[2];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pj = exp2f(sv[j] - mu);
+      const float pj = __builtin_amdgcn_exp2f(sv[j] - mu);  // exp2(-inf) = 0 for masked keys
       psum += pj;
       pf[j >> 3][j & 7] = (__bf16)pj;
     }
@@ -357,18 +381,23 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
     // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
     // The transposed reads fetch V rows base..base+3 and base+8..base+11.
+    stage_latent(nxt, kvb, row_bytes, slot_cur, wave, lane, 3);
+    stage_rope(nxt, kvb, row_bytes, slot_cur, wave, lane);
 #pragma unroll
     for (int kh2 = 0; kh2 < 2; ++kh2) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow;
-        bf16x8_t va[4];
+        i16x4_t lo[4], hi[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + voff[0][db]));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TVMLA_LDS(i16x4_t, vb + voff[1][db]));
-          va[db] = cat4(lo, hi);
+          lo[db] = tr_read(vb + voff[0][db]);
+          hi[db] = tr_read(vb + voff[1][db]);
         }
+        lds_wait8(lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
+        bf16x8_t va[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va[db] = cat4(lo[db], hi[db]);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const bf16x8_t pb = as_bf16x8(pex[((x + 2 * kh2) * 2 + c) * 64 + lane]);
@@ -385,35 +414,40 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     body(tile, odd ? kb1 : kb0, odd ? kb0 : kb1);
   }
 
+  // The last tile's prefetch targeted the idle buffer; let it land before
+  // the workgroup can exit and release its LDS.
+  __builtin_amdgcn_s_waitcnt(0x0070);
+
   // ---- row sums: two wavefronts x two lane halves per row
   const float lt = l_part + __shfl_xor(l_part, 32, 64);
   lds_barrier();
   if (hf == 0) mex[wave * 32 + col] = lt;
   lds_barrier();
-  const float lrow[2] = {mex[col] + mex[64 + col], mex[32 + col] + mex[96 + col]};
+  const float lrow0 = mex[col] + mex[64 + col];
+  const float lrow1 = mex[32 + col] + mex[96 + col];
 
   // ---- partial results: entries [128 wave, +128) of both row blocks
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  auto write_block = [&](const f32x16_t (&ox)[4], float mref, float lrow, int x) {
     const int row = g * kRowsWG + 32 * x + col;
-    if (row >= R) continue;
+    if (row >= R) return;
     const size_t prow = ((size_t)b * p.nsplit + s) * R + row;
     float* dst = p.o_part + prow * kDLatent + 128 * wave + 4 * hf;
-    const float inv = lrow[x] > 0.f ? 1.f / lrow[x] : 0.f;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         float4 v;
-        v.x = o[x][db][4 * jg + 0] * inv;
-        v.y = o[x][db][4 * jg + 1] * inv;
-        v.z = o[x][db][4 * jg + 2] * inv;
-        v.w = o[x][db][4 * jg + 3] * inv;
+        v.x = ox[db][4 * jg + 0] * inv;
+        v.y = ox[db][4 * jg + 1] * inv;
+        v.z = ox[db][4 * jg + 2] * inv;
+        v.w = ox[db][4 * jg + 3] * inv;
         *reinterpret_cast<float4*>(dst + 32 * db + 8 * jg) = v;
       }
-    if (wave == 0 && hf == 0)
-      p.lse_part[prow] = lrow[x] > 0.f ? (m_ref[x] + log2f(lrow[x])) * kLn2 : -INFINITY;
-  }
+    if (wave == 0 && hf == 0) p.lse_part[prow] = lrow > 0.f ? (mref + log2f(lrow)) * kLn2 : -INFINITY;
+  };
+  write_block(o[0], m_ref0, lrow0, 0);
+  write_block(o[1], m_ref1, lrow1, 1);
 }
 
 }  // namespace
