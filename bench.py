@@ -40,11 +40,29 @@ def algorithmic(w):
     return dict(kv_bytes=kv_bytes, all_bytes=kv_bytes + meta_bytes + q_bytes + out_bytes, flops=flops)
 
 
-def cpu_baseline(w, pool_host, seconds_hint=10.0):
-    """Time the fp64 oracle on a row sample of the same workload (all heads of
-    the first draft tokens), scaled to the whole job's KV-read GB/s."""
-    import numpy as np
+def profiled_traffic():
+    """HBM bytes per split launch from the committed rocprofv3 summary, or None
+    if the split kernel's source has changed since those counters were taken."""
+    import hashlib
+    import re
 
+    prof = os.path.join(ROOT, "profiles", "split_mfma_long185k.md")
+    src = os.path.join(ROOT, "speculative_decoding_verify_mla_amd", "csrc", "split_mfma.hip")
+    try:
+        text = open(prof).read()
+        m = re.search(r"traffic_bytes_per_launch: fetch=(\d+) write=(\d+) source_sha256_prefix=([0-9a-f]+)", text)
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if not m or not cur.startswith(m.group(3)):
+        return None
+    return int(m.group(1)) + int(m.group(2))
+
+
+def cpu_baseline(w, pool_host):
+    """Time the fp64 oracle on the same workload on the host cores. The whole
+    job is the sample when it fits in about half a minute of CPU time;
+    otherwise the rows of the first draft tokens (all heads), scaled."""
     from oracle import verify_fp64 as vo
 
     try:
@@ -54,23 +72,28 @@ def cpu_baseline(w, pool_host, seconds_hint=10.0):
     except Exception:  # threadpoolctl missing: report the OMP setting
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     T, H = w.num_draft, w.num_heads
-    tokens = min(2, T)
-    picks = [(i, h) for i in range(tokens) for h in range(H)]
-    t0 = time.perf_counter()
-    vo.verify_rows(w.q_nope, w.q_rope, pool_host, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
-                   w.mask_indptr, w.sm_scale, T, picks)
-    dt = time.perf_counter() - t0
-    frac = len(picks) / float(w.batch * T * H)
+    rows = w.batch * T * H
     kv = algorithmic(w)["kv_bytes"]
+    whole = algorithmic(w)["flops"] <= 2e12  # ~0.5-2 TFLOP of fp64 BLAS: seconds to tens of seconds
+    t0 = time.perf_counter()
+    if whole:
+        vo.verify(w.q_nope, w.q_rope, pool_host, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
+                  w.mask_indptr, w.sm_scale, T)
+        frac, what = 1.0, f"the whole job ({rows} query rows x {w.total_keys} keys), oracle.verify"
+    else:
+        tokens = min(2, T)
+        picks = [(i, h) for i in range(tokens) for h in range(H)]
+        vo.verify_rows(w.q_nope, w.q_rope, pool_host, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
+                       w.mask_indptr, w.sm_scale, T, picks)
+        frac = len(picks) / float(rows)
+        what = f"oracle.verify_rows on {len(picks)} of {rows} query rows (draft tokens 0-{tokens - 1} of request 0)"
+    dt = time.perf_counter() - t0
     return {
-        "value": kv * frac / dt / 1e9,
+        "value": round(kv * frac / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"oracle.verify_rows on {len(picks)} of {w.batch * T * H} query rows "
-                  f"(draft tokens 0-{tokens - 1}, all {H} heads, request 0) in {dt:.2f} s; "
-                  f"value = KV bytes x {frac:.4f} / time",
-        "seconds": dt,
+        "sample": f"{what} in {dt:.2f} s; value = cache-row bytes x {frac:.4f} / time",
     }
 
 
@@ -206,7 +229,8 @@ def main(argv=None):
             "flops": alg["flops"],
         },
         "kernels_us": {"split": round(ms_split * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
-        "roofline": dict(roof, kernel="split", traffic=None),
+        "roofline": dict(roof, kernel="split",
+                         traffic=profiled_traffic() if args.workload == "long185k" and args.min_chunk == 0 else None),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
