@@ -49,6 +49,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 #define TVMLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
@@ -60,6 +61,7 @@ constexpr int kTileLat = kKT * kLatRow;
 constexpr int kTileBytes = kTileLat + kKT * kRopeRow;  // 73,728 bytes per tile buffer
 constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
 constexpr float kRescaleLog2 = 8.f;                    // lazy-rescale threshold (log2 units)
+constexpr int kRing = 6;                               // score operand reads in flight per wavefront
 
 // Piece swizzle of key k: a permutation of 0..15 over 16 consecutive keys
 // (the 16 lanes an LDS read cycle serves for the score operand) whose bits
@@ -86,7 +88,7 @@ __device__ __forceinline__ void tile_barrier() {
 // Transposed LDS read (ds_read_b64_tr_b16) issued through inline asm. The
 // compiler treats the builtin as touching any LDS location and would wait
 // for every in-flight direct-to-LDS load before it; here the caller waits
-// for the result explicitly with lds_wait8 before using it.
+// for the result explicitly (TVMLA_LDS_WAIT) before using it.
 __device__ __forceinline__ i16x4_t tr_read(const char* lds_ptr) {
   const uint32_t a = (uint32_t)(uintptr_t)TVMLA_LDS(const char, lds_ptr);
   i16x4_t r;
@@ -94,12 +96,69 @@ __device__ __forceinline__ i16x4_t tr_read(const char* lds_ptr) {
   return r;
 }
 
-// Wait for all outstanding LDS reads; the eight registers are tied to the
-// wait so no use of them can be scheduled before it.
-__device__ __forceinline__ void lds_wait8(i16x4_t& a0, i16x4_t& a1, i16x4_t& a2, i16x4_t& a3, i16x4_t& b0,
-                                          i16x4_t& b1, i16x4_t& b2, i16x4_t& b3) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+__device__ __forceinline__ u32x4_t lds_read128(const void* lds_ptr) {
+  const uint32_t a = (uint32_t)(uintptr_t)TVMLA_LDS(const char, lds_ptr);
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+
+// Wait for all outstanding LDS reads, with one value-product group's
+// operand registers (lo[4], hi[4], pb[2]) tied to the wait so no use of them
+// can be scheduled before it; TVMLA_PIN is the same ordering point without
+// the wait. Nothing else touches those registers between the asm reads and
+// the wait: they are the asm statements' own outputs and inputs.
+#define TVMLA_TIE10(lo, hi, pb)                                                                                 \
+  "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]), "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]), "+v"(hi[3]),        \
+      "+v"(pb[0]), "+v"(pb[1])
+#define TVMLA_LDS_WAIT(lo, hi, pb) asm volatile("s_waitcnt lgkmcnt(0)" : TVMLA_TIE10(lo, hi, pb))
+#define TVMLA_PIN(lo, hi, pb) asm volatile("" : TVMLA_TIE10(lo, hi, pb))
+
+// Score MFMA with the query operand read straight from AGPRs, where the
+// queries live for the whole split (the builtin would copy each operand to
+// VGPRs first). Back-to-back steps accumulate into the same registers, which
+// needs no wait states; TVMLA_MFMA_DRAIN adds the wait states an XDL result
+// needs before vector instructions may read it (the compiler cannot see
+// through the asm, so they are spelled out: 24, twice what 8 passes need).
+#define TVMLA_MFMA_QK_FIRST(acc, a, q) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(q))
+#define TVMLA_MFMA_QK(acc, a, q) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(q))
+#define TVMLA_MFMA_DRAIN(acc) asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc))
+
+// Score operand read (ds_read_b128) whose completion the caller waits for
+// with wait_lgkm_tied: "at most n LDS operations still outstanding", n being
+// the number of this wavefront's LDS reads issued after it. LDS operations
+// complete in order, so further LDS operations the compiler places in
+// between only make the wait stricter.
+__device__ __forceinline__ bf16x8_t frag_read(uint32_t lds_addr) {
+  bf16x8_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm_n(bf16x8_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
+}
+__device__ __forceinline__ void wait_lgkm_tied(bf16x8_t& r, int n) {
+  switch (n) {
+    case 0: wait_lgkm_n<0>(r); break;
+    case 1: wait_lgkm_n<1>(r); break;
+    case 2: wait_lgkm_n<2>(r); break;
+    case 3: wait_lgkm_n<3>(r); break;
+    case 4: wait_lgkm_n<4>(r); break;
+    case 5: wait_lgkm_n<5>(r); break;
+    case 6: wait_lgkm_n<6>(r); break;
+    default: wait_lgkm_n<7>(r); break;
+  }
+}
+
+// An opaque copy of a value: the compiler cannot see through it, so
+// addresses derived from it are computed where they are used instead of
+// being hoisted out of the tile loop and kept in registers for its whole
+// length.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -111,42 +170,37 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Direct-to-LDS loads of one 64-key tile into `dst` (issued in five pieces
-// spread over the previous tile's compute). slot_reg holds, in lane k, the
-// cache slot of the tile's key k.
-//   latent: key k = wave + 4u; a buffer resource over the key's cache row
-//           (scalar registers only; its 1152-byte size also bounds the read)
-//           and lane l loads piece l ^ swz(k) into LDS piece l of the key's
-//           1024-byte latent row;
-//   rope:   keys 8v..8v+7 (v = wave + 4u); lane l serves key 8v + l/8 and
-//           loads rope piece (l%8) ^ (swz & 7) into LDS piece l%8 of its row.
+// Direct-to-LDS loads of one 64-key tile into `dst`, spread one load at a
+// time over the previous tile's compute (a burst of loads would stall the
+// issuing wavefront until the texture path drains it). slot_reg holds, in
+// lane k, the cache slot of the tile's key k.
+//   latent: key k = wave + 4u (u = 0..15); a buffer resource over the key's
+//           cache row, whose address lane k holds in (ra_hi, ra_lo) (its
+//           1152-byte size also bounds the read), and lane l loads piece
+//           l ^ swz(k) into LDS piece l of the key's 1024-byte latent row;
+//   rope:   keys 8v..8v+7 (v = wave + 4u, u = 0..1); lane l serves key
+//           8v + l/8 and loads rope piece (l%8) ^ (swz & 7) into LDS piece
+//           l%8 of its row (source addresses from rope_source).
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
 
-// Latent loads for keys k = wave + 4u, u in [4 part, 4 part + 4).
-__device__ __forceinline__ void stage_latent(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
-                                             int lane, int part) {
-#pragma unroll
-  for (int u = 4 * part; u < 4 * part + 4; ++u) {
-    const int k = wave + 4 * u;
-    const int slot = __builtin_amdgcn_readlane(slot_reg, k);
-    const __amdgpu_buffer_rsrc_t row =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kv + (int64_t)slot * row_bytes), 0, kDKey * 2, kBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(row, TVMLA_LDS(void, dst + k * kLatRow), 16,
-                                             (lane ^ piece_swz(k)) << 4, 0, 0, 0);
-  }
+__device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
+  const int k = wave + 4 * u;
+  const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
+  const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)row_addr, 0, kDKey * 2, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(row, TVMLA_LDS(void, dst + k * kLatRow), 16, (lane ^ piece_swz(k)) << 4,
+                                           0, 0, 0);
 }
 
-// Rope loads: keys 8v..8v+7, v = wave + 4u.
-__device__ __forceinline__ void stage_rope(char* dst, const char* kv, int64_t row_bytes, int slot_reg, int wave,
-                                           int lane) {
-#pragma unroll
-  for (int u = 0; u < kKT / 32; ++u) {
-    const int v = wave + 4 * u;
-    const int k = 8 * v + (lane >> 3);
-    const int slot = __shfl(slot_reg, k, 64);
-    const char* src = kv + (int64_t)slot * row_bytes + kDLatent * 2 + (((lane & 7) ^ (piece_swz(k) & 7)) << 4);
-    __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
-  }
+__device__ __forceinline__ const char* rope_source(const char* kv, int64_t row_bytes, int slot_reg, int wave,
+                                                   int lane, int u) {
+  const int k = 8 * (wave + 4 * u) + (lane >> 3);
+  const int slot = __shfl(slot_reg, k, 64);
+  return kv + (int64_t)slot * row_bytes + kDLatent * 2 + (((lane & 7) ^ (piece_swz(k) & 7)) << 4);
+}
+
+__device__ __forceinline__ void stage_rope(char* dst, const char* src, int wave, int u) {
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + (wave + 4 * u) * 8 * kRopeRow), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -215,32 +269,31 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   float m_ref0 = -INFINITY, m_ref1 = -INFINITY;  // per row block: reference max (log2 units)
   float l_part = 0.f;                       // this lane's share of its scoring row's softmax sum
 
-  // Per-lane LDS byte offsets inside a tile buffer.
-  //   score operand (A of S^T = K Q^T): key qkey = 32kh + col, k-step ks
-  //   reads latent piece 2ks + hf at (2ks + hf) ^ swz(qkey); the XOR touches the low
-  //   four bits only, so the offset is 256 (ks / 8) + qoff[ks % 8]; rope
-  //   k-step 32 + b reads rope piece (2b + hf) ^ (swz(qkey) & 7).
-  const int qkey = 32 * kh + col;
-  const int sq = piece_swz(qkey);
-  int qoff[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) qoff[x] = qkey * kLatRow + (((2 * x + hf) ^ sq) << 4);
-  int roff[4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) roff[x] = kTileLat + qkey * kRopeRow + (((2 * x + hf) ^ (sq & 7)) << 4);
+  // Per-lane LDS byte offsets inside a tile buffer, recomputed per tile from
+  // an opaque copy of the lane index (an XOR and a shift each).
+  //   score operand (A of S^T = K Q^T): key qkey = 32kh + col; k-step ks
+  //   reads latent piece 2ks + hf, stored at (2ks + hf) ^ swz(qkey) =
+  //   2ks ^ sqh; rope k-step 32 + b reads rope piece (2b + hf) ^ (swz & 7).
   //   value operand (A of O^T += V^T P^T, transposed reads): lane group row
-  //   vr = (lane & 15) / 4 reads keys 32kh2 + 16c + 4hf + vr (+8), latent
-  //   entries d = 128w + 32db + 16g1 + 4(lane & 3) .. +3 (g1 = lane bit 4),
-  //   i.e. piece 16w + 4db + 2g1 + (lane & 3) / 2, byte 8 (lane & 1).
-  const int vr = 4 * hf + ((lane & 15) >> 2);
-  const int vpl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  int voff[2][4];  // [+8 keys][db]
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      voff[x][db] = (vr + 8 * x) * kLatRow + ((16 * wave + ((4 * db + vpl) ^ piece_swz(vr + 8 * x))) << 4) +
-                    8 * (lane & 1);
+  //   vr = (lane & 15) / 4 reads keys 32kh2 + 16c + 4hf + vr + 8x, latent
+  //   entries d = 128w + 32db + 16g1 + 4(lane & 3) .. +3 (g1 = lane bit 4):
+  //   piece 16w + 4db + vpl, vpl = 2g1 + (lane & 3) / 2, stored at
+  //   16w + ((4db + vpl) ^ swz(vr + 8x)) = 16w + (vt ^ 4db ^ 8x), vt = vpl ^ swz(vr).
+  struct LaneOffsets {
+    int qbase, rbase, sqh, vbase, vt;
+  };
+  auto lane_offsets = [&](int ln) -> LaneOffsets {
+    const int lhf = ln >> 5, lcol = ln & 31;
+    const int qk = 32 * kh + lcol;
+    const int vr = 4 * lhf + ((ln & 15) >> 2);
+    LaneOffsets L;
+    L.qbase = qk * kLatRow;
+    L.rbase = kTileLat + qk * kRopeRow;
+    L.sqh = piece_swz(qk) ^ lhf;
+    L.vbase = vr * kLatRow + 256 * wave + 8 * (ln & 1);
+    L.vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
+    return L;
+  };
 
   const float scale2 = p.sm_scale * kLog2e;
   const char* kvb = static_cast<const char*>(p.kv);
@@ -292,9 +345,19 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
 
   const int ntiles = (end - start + kKT - 1) / kKT;
   int slot_reg = slot_of(start + lane);
+  auto row_address = [&](int slot, uint32_t& lo, uint32_t& hi) {
+    const uint64_t a = (uint64_t)(uintptr_t)(kvb + (int64_t)slot * row_bytes);
+    lo = (uint32_t)a;
+    hi = (uint32_t)(a >> 32);
+  };
+  {
+    uint32_t lo, hi;
+    row_address(slot_reg, lo, hi);
 #pragma unroll
-  for (int part = 0; part < 4; ++part) stage_latent(kb0, kvb, row_bytes, slot_reg, wave, lane, part);
-  stage_rope(kb0, kvb, row_bytes, slot_reg, wave, lane);
+    for (int u = 0; u < kKT / 4; ++u) stage_key(kb0, lo, hi, wave, lane, u);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) stage_rope(kb0, rope_source(kvb, row_bytes, slot_reg, wave, lane, u), wave, u);
   load_mask(start);
   slot_reg = slot_of(start + kKT + lane);
 
@@ -312,6 +375,8 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   auto body = [&](int tile, const char* cur, char* nxt) {
     const int p0 = start + tile * kKT;
     tile_barrier();  // tile in LDS; every wavefront is done with the previous one
+    const int ln = opaque(lane);
+    const LaneOffsets L = lane_offsets(ln);
     // score register j of lane half hf holds tile key 32kh + 8(j/4) + 4hf + j%4
     const uint32_t vis = visible_bits(p0) >> (4 * hf);
     // Prefetch for the next tiles. On the last tile these re-read clamped,
@@ -319,26 +384,39 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     load_mask(p0 + kKT);
     const int slot_cur = slot_reg;
     slot_reg = slot_of(p0 + 2 * kKT + lane);
+    uint32_t ra_lo, ra_hi;  // lane k: cache row address of the next tile's key k
+    row_address(slot_cur, ra_lo, ra_hi);
+    // Rope sources of the next tile, resolved now (the lane shuffle is an LDS
+    // operation whose wait would otherwise land among the operand reads).
+    const char* rsrc0 = rope_source(kvb, row_bytes, slot_cur, wave, ln, 0);
+    const char* rsrc1 = rope_source(kvb, row_bytes, slot_cur, wave, ln, 1);
+    asm volatile("" : "+v"(rsrc0), "+v"(rsrc1));
 
     // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb.
-    // The four k-steps ahead are read into a ring of operand registers so
-    // each MFMA's LDS read was issued four MFMAs earlier; the next tile's
-    // loads are issued in three groups of four keys between the MFMAs.
-    auto kfrag = [&](int ks) -> bf16x8_t {
-      const int off = ks < 32 ? qoff[ks & 7] + 256 * (ks >> 3) : roff[ks - 32];
-      return *reinterpret_cast<const bf16x8_t*>(cur + off);
+    // The kRing k-steps ahead are read into a ring of operand registers so
+    // each MFMA's LDS read was issued kRing MFMAs earlier; twelve of the next
+    // tile's key loads go one every third MFMA.
+    const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
+    auto kaddr = [&](int ks) -> uint32_t {
+      return cur_lds + (ks < 32 ? L.qbase + (((2 * ks) ^ L.sqh) << 4)
+                                : L.rbase + (((2 * (ks - 32)) ^ (L.sqh & 7)) << 4));
     };
-    bf16x8_t ring[4];
+    bf16x8_t ring[kRing];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) ring[x] = kfrag(x);
-    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    f32x16_t sacc = zero;
+    for (int x = 0; x < kRing; ++x) ring[x] = frag_read(kaddr(x));
+    f32x16_t sacc;
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
-      if (ks % 12 == 0) stage_latent(nxt, kvb, row_bytes, slot_cur, wave, lane, ks / 12);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks & 3], qf[ks], sacc, 0, 0, 0);
-      if (ks + 4 < kQSteps) ring[ks & 3] = kfrag(ks + 4);
+      if (ks % 3 == 1) stage_key(nxt, ra_lo, ra_hi, wave, ln, ks / 3);
+      bf16x8_t& kf = ring[ks % kRing];
+      wait_lgkm_tied(kf, min(kRing - 1, kQSteps - 1 - ks));
+      if (ks == 0)
+        TVMLA_MFMA_QK_FIRST(sacc, kf, qf[0]);
+      else
+        TVMLA_MFMA_QK(sacc, kf, qf[ks]);
+      if (ks + kRing < kQSteps) kf = frag_read(kaddr(ks + kRing));
     }
+    TVMLA_MFMA_DRAIN(sacc);
 
     // ---- row maxima over the whole 64-key tile (two wavefronts per row block)
     float sv[16];
@@ -381,32 +459,68 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
     // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
     // The transposed reads fetch V rows base..base+3 and base+8..base+11.
-    stage_latent(nxt, kvb, row_bytes, slot_cur, wave, lane, 3);
-    stage_rope(nxt, kvb, row_bytes, slot_cur, wave, lane);
+    // Four operand groups g = (kh2, c): eight transposed V^T reads (four
+    // 32-entry blocks x two key quads) and the two P^T operands (one per row
+    // block). Group g+1's reads are issued before group g's eight MFMAs.
+    i16x4_t loA[4], hiA[4], loB[4], hiB[4];
+    u32x4_t pbA[2], pbB[2];
+    auto issue = [&](int grp, i16x4_t* lo, i16x4_t* hi, u32x4_t* pb) {
+      const int kh2 = grp >> 1, c = grp & 1;
+      const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow + L.vbase;
 #pragma unroll
-    for (int kh2 = 0; kh2 < 2; ++kh2) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow;
-        i16x4_t lo[4], hi[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          lo[db] = tr_read(vb + voff[0][db]);
-          hi[db] = tr_read(vb + voff[1][db]);
-        }
-        lds_wait8(lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
-        bf16x8_t va[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) va[db] = cat4(lo[db], hi[db]);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const bf16x8_t pb = as_bf16x8(pex[((x + 2 * kh2) * 2 + c) * 64 + lane]);
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-            o[x][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb, o[x][db], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) {
+        lo[db] = tr_read(vb + ((L.vt ^ (4 * db)) << 4));
+        hi[db] = tr_read(vb + 8 * kLatRow + ((L.vt ^ (4 * db) ^ 8) << 4));
       }
-    }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) pb[x] = lds_read128(&pex[((x + 2 * kh2) * 2 + c) * 64 + ln]);
+    };
+    auto product = [&](const i16x4_t* lo, const i16x4_t* hi, const u32x4_t* pb) {
+      bf16x8_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[db] = cat4(lo[db], hi[db]);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const bf16x8_t pbx = __builtin_bit_cast(bf16x8_t, pb[x]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[x][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pbx, o[x][db], 0, 0, 0);
+      }
+    };
+    // The scheduling barriers keep each group's MFMAs between the waits
+    // (the compiler may otherwise hoist the next wait above them).
+    // The rest of the next tile's loads go one or two per group.
+    stage_key(nxt, ra_lo, ra_hi, wave, ln, 12);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, loA, hiA, pbA);
+    TVMLA_LDS_WAIT(loA, hiA, pbA);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_key(nxt, ra_lo, ra_hi, wave, ln, 13);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, loB, hiB, pbB);
+    TVMLA_PIN(loA, hiA, pbA);
+    product(loA, hiA, pbA);
+    __builtin_amdgcn_sched_barrier(0);
+    TVMLA_LDS_WAIT(loB, hiB, pbB);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_key(nxt, ra_lo, ra_hi, wave, ln, 14);
+    stage_rope(nxt, rsrc0, wave, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(2, loA, hiA, pbA);
+    TVMLA_PIN(loB, hiB, pbB);
+    product(loB, hiB, pbB);
+    __builtin_amdgcn_sched_barrier(0);
+    TVMLA_LDS_WAIT(loA, hiA, pbA);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_key(nxt, ra_lo, ra_hi, wave, ln, 15);
+    stage_rope(nxt, rsrc1, wave, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(3, loB, hiB, pbB);
+    TVMLA_PIN(loA, hiA, pbA);
+    product(loA, hiA, pbA);
+    __builtin_amdgcn_sched_barrier(0);
+    TVMLA_LDS_WAIT(loB, hiB, pbB);
+    product(loB, hiB, pbB);
   };
 
   for (int tile = 0; tile < ntiles; ++tile) {
