@@ -62,7 +62,8 @@ typedef enum {
   TVMLA_E_WORKSPACE = 4, /* workspace NULL or smaller than tvmla_workspace_bytes */
   TVMLA_E_ALIGN = 5,     /* a pointer or stride breaks the alignment rules       */
   TVMLA_E_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch             */
-  TVMLA_E_ALGO = 7       /* unknown algorithm selector                           */
+  TVMLA_E_ALGO = 7,      /* unknown algorithm selector                           */
+  TVMLA_E_VALUE = 8      /* sm_scale is not a finite positive number              */
 } tvmla_status;
 
 typedef enum {
@@ -105,7 +106,8 @@ size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads
  * custom_mask   uint8, per request a row-major [num_draft][N_b] block at
  *               offset mask_indptr[b]; nonzero = visible
  * mask_indptr   int32 [batch+1]
- * sm_scale      multiplies the full 576-wide dot product
+ * sm_scale      multiplies the full 576-wide dot product; must be finite
+ *               and positive (a softmax temperature), else TVMLA_E_VALUE
  * nsplit        splits per request: split s covers keys
  *               [s*chunk, min((s+1)*chunk, N_b)), chunk = ceil(N_b/nsplit)
  *               (page 1, "The NSPLIT Calculation"); empty splits return at

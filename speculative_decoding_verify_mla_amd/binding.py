@@ -27,6 +27,7 @@ STATUS = {
     5: "TVMLA_E_ALIGN",
     6: "TVMLA_E_LAUNCH",
     7: "TVMLA_E_ALGO",
+    8: "TVMLA_E_VALUE",
 }
 
 # every symbol include/tvmla.h declares

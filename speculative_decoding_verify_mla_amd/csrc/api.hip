@@ -44,6 +44,7 @@ const char* tvmla_status_str(int32_t status) {
     case TVMLA_E_ALIGN: return "pointer or stride misaligned";
     case TVMLA_E_LAUNCH: return "kernel launch failed";
     case TVMLA_E_ALGO: return "unknown algorithm";
+    case TVMLA_E_VALUE: return "sm_scale must be finite and positive";
     default: return "unknown status";
   }
 }
@@ -72,6 +73,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
   if (st != TVMLA_OK) return st;
   if (min_chunk < 0) return TVMLA_E_SHAPE;
+  if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return TVMLA_E_VALUE;
   if (kv_stride_row < TVMLA_D_KEY) return TVMLA_E_SHAPE;
   if (q_nope_stride_tok < 0 || q_nope_stride_head < 0 || q_rope_stride_tok < 0 || q_rope_stride_head < 0)
     return TVMLA_E_SHAPE;

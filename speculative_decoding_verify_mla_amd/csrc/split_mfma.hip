@@ -324,12 +324,16 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   auto load_mask = [&](int p0) {
     int key = p0 + 32 * kh + col;
     key = key < end ? key : end - 1;
+    mnext[0] = mbase[key];
+    if (ntok > 1) {  // blocks of one token (at least 32 heads) need one byte
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mnext[u] = mbase[(int64_t)min(u, ntok - 1) * N + key];
+      for (int u = 1; u < 4; ++u) mnext[u] = mbase[(int64_t)min(u, ntok - 1) * N + key];
+    }
   };
   auto visible_bits = [&](int p0) -> uint32_t {  // bit k: tile key 32kh + k visible to my row
     const int key = p0 + 32 * kh + col;
     const bool kok = key < end;
+    if (ntok == 1) return (uint32_t)__ballot(kok && mnext[0] != 0);
     uint32_t mine = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -418,15 +422,27 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     }
     TVMLA_MFMA_DRAIN(sacc);
 
-    // ---- row maxima over the whole 64-key tile (two wavefronts per row block)
-    float sv[16];
-    float tm = -INFINITY;
+    // ---- row maxima over the whole 64-key tile (two wavefronts per row block).
+    // Masked scores become -inf; when every score of the wavefront is
+    // visible (the common case) the selects are skipped. sm_scale > 0, so the
+    // maximum of the raw scores times scale2 is the maximum of the scaled
+    // scores, exactly (rounding is monotonic).
+    float sm[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      sv[j] = ((vis >> (8 * (j >> 2) + (j & 3))) & 1u) ? sacc[j] * scale2 : -INFINITY;
-      tm = fmaxf(tm, sv[j]);
+    for (int j = 0; j < 16; ++j) sm[j] = sacc[j];
+    constexpr uint32_t kVisAll = 0x0F0F0F0Fu;  // bits 8(j/4) + j%4, j = 0..15
+    if (__ballot((vis & kVisAll) != kVisAll)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sm[j] = ((vis >> (8 * (j >> 2) + (j & 3))) & 1u) ? sm[j] : -INFINITY;
     }
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    float tm = sm[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) tm = fmaxf(tm, sm[j]);
+    {
+      // both lane halves hold the same rows: swap halves and combine
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+    }
     if (hf == 0) mex[wave * 32 + col] = tm;
     lds_barrier();
     const float tm0 = fmaxf(mex[col], mex[64 + col]);       // row block 0: wavefronts 0, 2
@@ -438,18 +454,19 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
       rescale(o[1], m_ref1, rb == 1, tm1);
     }
 
-    // ---- probabilities of this wavefront's 32 keys x 32 rows
+    // ---- probabilities of this wavefront's 32 keys x 32 rows:
+    // exp2(s * scale2 - m_ref), one fma each; exp2(-inf) = 0 for masked keys
     float mu = rb == 0 ? m_ref0 : m_ref1;
-    mu = mu == -INFINITY ? 0.f : mu;
+    mu = mu == -INFINITY ? 0.f : -mu;
     bf16x8_t pf[2];
-    float psum = 0.f;
+    float pj[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pj = __builtin_amdgcn_exp2f(sv[j] - mu);  // exp2(-inf) = 0 for masked keys
-      psum += pj;
-      pf[j >> 3][j & 7] = (__bf16)pj;
+      pj[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[j], scale2, mu));
+      pf[j >> 3][j & 7] = (__bf16)pj[j];
     }
-    l_part += psum;
+    l_part += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7])) +
+              (((pj[8] + pj[9]) + (pj[10] + pj[11])) + ((pj[12] + pj[13]) + (pj[14] + pj[15])));
     pex[(wave * 2 + 0) * 64 + lane] = as_u4(pf[0]);
     pex[(wave * 2 + 1) * 64 + lane] = as_u4(pf[1]);
     lds_barrier();

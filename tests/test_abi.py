@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert binding.version() >= 100
-    for code in range(8):
+    for code in range(9):
         s = binding.status_str(code)
         assert isinstance(s, str) and s
     assert binding.status_str(99) == "unknown status"
@@ -107,6 +107,11 @@ def test_bad_dtype(lib, kw):
 
 def test_bad_algo(lib):
     assert _call(lib, algo=3) == 7
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.07, float("inf"), float("nan")])
+def test_bad_scale(lib, scale):
+    assert _call(lib, scale=scale) == 8
 
 
 @pytest.mark.parametrize("kw", [dict(q_nope=_FAKE + 8), dict(kv=_FAKE + 2), dict(out=_FAKE + 4), dict(ws=_FAKE + 8),
