@@ -56,7 +56,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kRowsWG = 64;   // query rows per workgroup (2 blocks of 32)
 constexpr int kKT = 64;       // keys per tile (2 halves of 32)
 constexpr int kLatRow = 1024; // bytes of one key's latent part in LDS (64 pieces of 16 B)
-constexpr int kRopeRow = 128; // bytes of one key's rope part in LDS (8 pieces)
+constexpr int kRopeRow = 128; // bytes of one key's rope part in LDS (8 pieces of 16 B)
 constexpr int kTileLat = kKT * kLatRow;
 constexpr int kTileBytes = kTileLat + kKT * kRopeRow;  // 73,728 bytes per tile buffer
 constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
@@ -174,17 +174,19 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 // time over the previous tile's compute (a burst of loads would stall the
 // issuing wavefront until the texture path drains it). slot_reg holds, in
 // lane k, the cache slot of the tile's key k.
-//   latent: key k = wave + 4u (u = 0..15); a buffer resource over the key's
+//   latent: key k = 16 wave + u (u = 0..15); a buffer resource over the key's
 //           cache row, whose address lane k holds in (ra_hi, ra_lo) (its
 //           1152-byte size also bounds the read), and lane l loads piece
 //           l ^ swz(k) into LDS piece l of the key's 1024-byte latent row;
-//   rope:   keys 8v..8v+7 (v = wave + 4u, u = 0..1); lane l serves key
-//           8v + l/8 and loads rope piece (l%8) ^ (swz & 7) into LDS piece
-//           l%8 of its row (source addresses from rope_source).
+//   rope:   stored piece-major: rope piece q (8 entries) of key k at
+//           q * 1024 + 16k of the rope region. Load q = 2 wave + u (u = 0..1)
+//           has lane k fetch piece q of key k from its own row address, so
+//           no lane exchange is needed; the score reads of one piece then
+//           cover 32 consecutive keys (conflict-free without a swizzle).
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
 
 __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
-  const int k = wave + 4 * u;
+  const int k = 16 * wave + u;  // swz(k) depends on u only
   const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
   const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)row_addr, 0, kDKey * 2, kBufferWord3);
@@ -192,15 +194,10 @@ __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra
                                            0, 0, 0);
 }
 
-__device__ __forceinline__ const char* rope_source(const char* kv, int64_t row_bytes, int slot_reg, int wave,
-                                                   int lane, int u) {
-  const int k = 8 * (wave + 4 * u) + (lane >> 3);
-  const int slot = __shfl(slot_reg, k, 64);
-  return kv + (int64_t)slot * row_bytes + kDLatent * 2 + (((lane & 7) ^ (piece_swz(k) & 7)) << 4);
-}
-
-__device__ __forceinline__ void stage_rope(char* dst, const char* src, int wave, int u) {
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + (wave + 4 * u) * 8 * kRopeRow), 16, 0, 0);
+__device__ __forceinline__ void stage_rope(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int u) {
+  const int q = 2 * wave + u;
+  const char* src = reinterpret_cast<const char*>(((uint64_t)ra_hi << 32) | ra_lo) + kDLatent * 2 + 16 * q;
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + q * kKT * 16), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -273,7 +270,8 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   // an opaque copy of the lane index (an XOR and a shift each).
   //   score operand (A of S^T = K Q^T): key qkey = 32kh + col; k-step ks
   //   reads latent piece 2ks + hf, stored at (2ks + hf) ^ swz(qkey) =
-  //   2ks ^ sqh; rope k-step 32 + b reads rope piece (2b + hf) ^ (swz & 7).
+  //   2ks ^ sqh; rope k-step 32 + b reads rope piece 2b + hf of key qkey,
+  //   at rbase + 2b * 1024.
   //   value operand (A of O^T += V^T P^T, transposed reads): lane group row
   //   vr = (lane & 15) / 4 reads keys 32kh2 + 16c + 4hf + vr + 8x, latent
   //   entries d = 128w + 32db + 16g1 + 4(lane & 3) .. +3 (g1 = lane bit 4):
@@ -288,7 +286,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     const int vr = 4 * lhf + ((ln & 15) >> 2);
     LaneOffsets L;
     L.qbase = qk * kLatRow;
-    L.rbase = kTileLat + qk * kRopeRow;
+    L.rbase = kTileLat + lhf * kKT * 16 + qk * 16;
     L.sqh = piece_swz(qk) ^ lhf;
     L.vbase = vr * kLatRow + 256 * wave + 8 * (ln & 1);
     L.vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
@@ -359,9 +357,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     row_address(slot_reg, lo, hi);
 #pragma unroll
     for (int u = 0; u < kKT / 4; ++u) stage_key(kb0, lo, hi, wave, lane, u);
-  }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) stage_rope(kb0, rope_source(kvb, row_bytes, slot_reg, wave, lane, u), wave, u);
+    for (int u = 0; u < 2; ++u) stage_rope(kb0, lo, hi, wave, u);
+  }
   load_mask(start);
   slot_reg = slot_of(start + kKT + lane);
 
@@ -390,20 +388,15 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     slot_reg = slot_of(p0 + 2 * kKT + lane);
     uint32_t ra_lo, ra_hi;  // lane k: cache row address of the next tile's key k
     row_address(slot_cur, ra_lo, ra_hi);
-    // Rope sources of the next tile, resolved now (the lane shuffle is an LDS
-    // operation whose wait would otherwise land among the operand reads).
-    const char* rsrc0 = rope_source(kvb, row_bytes, slot_cur, wave, ln, 0);
-    const char* rsrc1 = rope_source(kvb, row_bytes, slot_cur, wave, ln, 1);
-    asm volatile("" : "+v"(rsrc0), "+v"(rsrc1));
 
     // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb.
     // The kRing k-steps ahead are read into a ring of operand registers so
-    // each MFMA's LDS read was issued kRing MFMAs earlier; twelve of the next
-    // tile's key loads go one every third MFMA.
+    // each MFMA's LDS read was issued kRing MFMAs earlier. All eighteen of
+    // the next tile's loads go here, one every second MFMA: the value product
+    // below reads LDS harder, and loads issued there cost more.
     const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
     auto kaddr = [&](int ks) -> uint32_t {
-      return cur_lds + (ks < 32 ? L.qbase + (((2 * ks) ^ L.sqh) << 4)
-                                : L.rbase + (((2 * (ks - 32)) ^ (L.sqh & 7)) << 4));
+      return cur_lds + (ks < 32 ? L.qbase + (((2 * ks) ^ L.sqh) << 4) : L.rbase + 2 * (ks - 32) * kKT * 16);
     };
     bf16x8_t ring[kRing];
 #pragma unroll
@@ -411,7 +404,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     f32x16_t sacc;
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
-      if (ks % 3 == 1) stage_key(nxt, ra_lo, ra_hi, wave, ln, ks / 3);
+      if (ks % 2 == 1 && ks < 32) stage_key(nxt, ra_lo, ra_hi, wave, ln, ks / 2);
+      if (ks == 33) stage_rope(nxt, ra_lo, ra_hi, wave, 0);
+      if (ks == 35) stage_rope(nxt, ra_lo, ra_hi, wave, 1);
       bf16x8_t& kf = ring[ks % kRing];
       wait_lgkm_tied(kf, min(kRing - 1, kQSteps - 1 - ks));
       if (ks == 0)
@@ -506,32 +501,18 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     };
     // The scheduling barriers keep each group's MFMAs between the waits
     // (the compiler may otherwise hoist the next wait above them).
-    // The rest of the next tile's loads go one or two per group.
-    stage_key(nxt, ra_lo, ra_hi, wave, ln, 12);
-    __builtin_amdgcn_sched_barrier(0);
     issue(0, loA, hiA, pbA);
     TVMLA_LDS_WAIT(loA, hiA, pbA);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_key(nxt, ra_lo, ra_hi, wave, ln, 13);
-    __builtin_amdgcn_sched_barrier(0);
     issue(1, loB, hiB, pbB);
     TVMLA_PIN(loA, hiA, pbA);
     product(loA, hiA, pbA);
     __builtin_amdgcn_sched_barrier(0);
     TVMLA_LDS_WAIT(loB, hiB, pbB);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_key(nxt, ra_lo, ra_hi, wave, ln, 14);
-    stage_rope(nxt, rsrc0, wave, 0);
-    __builtin_amdgcn_sched_barrier(0);
     issue(2, loA, hiA, pbA);
     TVMLA_PIN(loB, hiB, pbB);
     product(loB, hiB, pbB);
     __builtin_amdgcn_sched_barrier(0);
     TVMLA_LDS_WAIT(loA, hiA, pbA);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_key(nxt, ra_lo, ra_hi, wave, ln, 15);
-    stage_rope(nxt, rsrc1, wave, 1);
-    __builtin_amdgcn_sched_barrier(0);
     issue(3, loB, hiB, pbB);
     TVMLA_PIN(loA, hiA, pbA);
     product(loA, hiA, pbA);
