@@ -178,11 +178,12 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 //           cache row, whose address lane k holds in (ra_hi, ra_lo) (its
 //           1152-byte size also bounds the read), and lane l loads piece
 //           l ^ swz(k) into LDS piece l of the key's 1024-byte latent row;
-//   rope:   stored piece-major: rope piece q (8 entries) of key k at
-//           q * 1024 + 16k of the rope region. Load q = 2 wave + u (u = 0..1)
-//           has lane k fetch piece q of key k from its own row address, so
-//           no lane exchange is needed; the score reads of one piece then
-//           cover 32 consecutive keys (conflict-free without a swizzle).
+//   rope:   keys 8v..8v+7 (v = 2 wave + u, u = 0..1), 128 contiguous bytes
+//           each: lane l serves key k = 8v + l/8 and stores its 16-byte
+//           piece (l%8) ^ (k%8) at position l%8 of the key's 128-byte rope
+//           row, so a score read of one piece over 8 consecutive keys hits
+//           8 different bank groups. `row` is lane l's source row, the
+//           cache row of key k (fetched from lane k with a lane shuffle).
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
 
 __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
@@ -194,10 +195,10 @@ __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra
                                            0, 0, 0);
 }
 
-__device__ __forceinline__ void stage_rope(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int u) {
-  const int q = 2 * wave + u;
-  const char* src = reinterpret_cast<const char*>(((uint64_t)ra_hi << 32) | ra_lo) + kDLatent * 2 + 16 * q;
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + q * kKT * 16), 16, 0, 0);
+__device__ __forceinline__ void stage_rope(char* dst, const char* row, int wave, int lane, int u) {
+  const int v = 2 * wave + u;
+  const char* src = row + kDLatent * 2 + 16 * ((lane & 7) ^ (lane >> 3));
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -271,14 +272,14 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   //   score operand (A of S^T = K Q^T): key qkey = 32kh + col; k-step ks
   //   reads latent piece 2ks + hf, stored at (2ks + hf) ^ swz(qkey) =
   //   2ks ^ sqh; rope k-step 32 + b reads rope piece 2b + hf of key qkey,
-  //   at rbase + 2b * 1024.
+  //   stored at position (2b + hf) ^ (qkey % 8) = 2b ^ rsw of its row.
   //   value operand (A of O^T += V^T P^T, transposed reads): lane group row
   //   vr = (lane & 15) / 4 reads keys 32kh2 + 16c + 4hf + vr + 8x, latent
   //   entries d = 128w + 32db + 16g1 + 4(lane & 3) .. +3 (g1 = lane bit 4):
   //   piece 16w + 4db + vpl, vpl = 2g1 + (lane & 3) / 2, stored at
   //   16w + ((4db + vpl) ^ swz(vr + 8x)) = 16w + (vt ^ 4db ^ 8x), vt = vpl ^ swz(vr).
   struct LaneOffsets {
-    int qbase, rbase, sqh, vbase, vt;
+    int qbase, rbase, sqh, rsw, vbase, vt;
   };
   auto lane_offsets = [&](int ln) -> LaneOffsets {
     const int lhf = ln >> 5, lcol = ln & 31;
@@ -286,7 +287,8 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     const int vr = 4 * lhf + ((ln & 15) >> 2);
     LaneOffsets L;
     L.qbase = qk * kLatRow;
-    L.rbase = kTileLat + lhf * kKT * 16 + qk * 16;
+    L.rbase = kTileLat + qk * kRopeRow;
+    L.rsw = lhf ^ (qk & 7);
     L.sqh = piece_swz(qk) ^ lhf;
     L.vbase = vr * kLatRow + 256 * wave + 8 * (ln & 1);
     L.vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
@@ -358,7 +360,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
 #pragma unroll
     for (int u = 0; u < kKT / 4; ++u) stage_key(kb0, lo, hi, wave, lane, u);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) stage_rope(kb0, lo, hi, wave, u);
+    for (int u = 0; u < 2; ++u)
+      stage_rope(kb0, kvb + (int64_t)__shfl(slot_reg, 8 * (2 * wave + u) + (lane >> 3), 64) * row_bytes, wave, lane,
+                 u);
   }
   load_mask(start);
   slot_reg = slot_of(start + kKT + lane);
@@ -388,6 +392,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     slot_reg = slot_of(p0 + 2 * kKT + lane);
     uint32_t ra_lo, ra_hi;  // lane k: cache row address of the next tile's key k
     row_address(slot_cur, ra_lo, ra_hi);
+    // slots of the next tile's rope keys 8(2 wave + u) + lane/8
+    const int rslot0 = __shfl(slot_cur, 16 * wave + (ln >> 3), 64);
+    const int rslot1 = __shfl(slot_cur, 16 * wave + 8 + (ln >> 3), 64);
 
     // ---- S^T = K Q^T: keys 32kh.. of the tile x the 32 rows of block rb.
     // The kRing k-steps ahead are read into a ring of operand registers so
@@ -396,7 +403,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     // below reads LDS harder, and loads issued there cost more.
     const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
     auto kaddr = [&](int ks) -> uint32_t {
-      return cur_lds + (ks < 32 ? L.qbase + (((2 * ks) ^ L.sqh) << 4) : L.rbase + 2 * (ks - 32) * kKT * 16);
+      return cur_lds + (ks < 32 ? L.qbase + (((2 * ks) ^ L.sqh) << 4) : L.rbase + (((2 * (ks - 32)) ^ L.rsw) << 4));
     };
     bf16x8_t ring[kRing];
 #pragma unroll
@@ -405,8 +412,6 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
       if (ks % 2 == 1 && ks < 32) stage_key(nxt, ra_lo, ra_hi, wave, ln, ks / 2);
-      if (ks == 33) stage_rope(nxt, ra_lo, ra_hi, wave, 0);
-      if (ks == 35) stage_rope(nxt, ra_lo, ra_hi, wave, 1);
       bf16x8_t& kf = ring[ks % kRing];
       wait_lgkm_tied(kf, min(kRing - 1, kQSteps - 1 - ks));
       if (ks == 0)
@@ -415,6 +420,9 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
         TVMLA_MFMA_QK(sacc, kf, qf[ks]);
       if (ks + kRing < kQSteps) kf = frag_read(kaddr(ks + kRing));
     }
+    // Rope loads after the last operand wait, so the shuffles' wait is free.
+    stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
+    stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
     TVMLA_MFMA_DRAIN(sacc);
 
     // ---- row maxima over the whole 64-key tile (two wavefronts per row block).
