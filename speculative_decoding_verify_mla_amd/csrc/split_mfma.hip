@@ -113,6 +113,7 @@ __device__ __forceinline__ u32x4_t lds_read128(const void* lds_ptr) {
       "+v"(pb[0]), "+v"(pb[1])
 #define TVMLA_LDS_WAIT(lo, hi, pb) asm volatile("s_waitcnt lgkmcnt(0)" : TVMLA_TIE10(lo, hi, pb))
 #define TVMLA_PIN(lo, hi, pb) asm volatile("" : TVMLA_TIE10(lo, hi, pb))
+#define TVMLA_LDS_WAIT_F(lo, hi, pb, f) asm volatile("s_waitcnt lgkmcnt(0)" : TVMLA_TIE10(lo, hi, pb), "+v"(f))
 
 // Score MFMA with the query operand read straight from AGPRs, where the
 // queries live for the whole split (the builtin would copy each operand to
@@ -207,6 +208,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   __shared__ __attribute__((aligned(16))) char kb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint4 pex[4 * 2 * 64];  // P^T operands: [wave][k-step][lane]
   __shared__ float mex[4 * 32];                                   // per-wavefront row maxima / sums
+  __shared__ __attribute__((aligned(16))) int rescale_flag[4];    // per wavefront: a row outgrew m_ref
 
   // Workgroup ids reach the 8 XCDs round-robin (id % 8). Every row group of
   // one (request, split) pair gets the same id % 8, so the pair's key rows
@@ -425,6 +427,49 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
     TVMLA_MFMA_DRAIN(sacc);
 
+    // ---- O^T += V^T P^T for latent entries [128 wave, +128), both row blocks
+    // (defined here: group 0's V^T reads are issued before the softmax).
+    // Output register j of the score MFMA in lane half hf holds key
+    // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
+    // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
+    // The transposed reads fetch V rows base..base+3 and base+8..base+11.
+    // Four operand groups g = (kh2, c): eight transposed V^T reads (four
+    // 32-entry blocks x two key quads) and the two P^T operands (one per row
+    // block). Group g+1's reads are issued before group g's eight MFMAs.
+    i16x4_t loA[4], hiA[4], loB[4], hiB[4];
+    u32x4_t pbA[2], pbB[2];
+    auto issue_v = [&](int grp, i16x4_t* lo, i16x4_t* hi) {
+      const int kh2 = grp >> 1, c = grp & 1;
+      const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow + L.vbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        lo[db] = tr_read(vb + ((L.vt ^ (4 * db)) << 4));
+        hi[db] = tr_read(vb + 8 * kLatRow + ((L.vt ^ (4 * db) ^ 8) << 4));
+      }
+    };
+    auto issue_p = [&](int grp, u32x4_t* pb) {
+      const int kh2 = grp >> 1, c = grp & 1;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) pb[x] = lds_read128(&pex[((x + 2 * kh2) * 2 + c) * 64 + ln]);
+    };
+    auto issue = [&](int grp, i16x4_t* lo, i16x4_t* hi, u32x4_t* pb) {
+      issue_v(grp, lo, hi);
+      issue_p(grp, pb);
+    };
+    auto product = [&](const i16x4_t* lo, const i16x4_t* hi, const u32x4_t* pb) {
+      bf16x8_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[db] = cat4(lo[db], hi[db]);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const bf16x8_t pbx = __builtin_bit_cast(bf16x8_t, pb[x]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[x][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pbx, o[x][db], 0, 0, 0);
+      }
+    };
+    issue_v(0, loA, hiA);
+
     // ---- row maxima over the whole 64-key tile (two wavefronts per row block).
     // Masked scores become -inf; when every score of the wavefront is
     // visible (the common case) the selects are skipped. sm_scale > 0, so the
@@ -446,71 +491,54 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
       tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
     }
-    if (hf == 0) mex[wave * 32 + col] = tm;
-    lds_barrier();
-    const float tm0 = fmaxf(mex[col], mex[64 + col]);       // row block 0: wavefronts 0, 2
-    const float tm1 = fmaxf(mex[32 + col], mex[96 + col]);  // row block 1: wavefronts 1, 3
-    // Every wavefront sees the same maxima and the same m_ref, so all four
-    // take the same decision and keep identical references.
-    if (__ballot(tm0 > m_ref0 + kRescaleLog2 || tm1 > m_ref1 + kRescaleLog2)) {
-      rescale(o[0], m_ref0, rb == 0, tm0);
-      rescale(o[1], m_ref1, rb == 1, tm1);
-    }
-
-    // ---- probabilities of this wavefront's 32 keys x 32 rows:
-    // exp2(s * scale2 - m_ref), one fma each; exp2(-inf) = 0 for masked keys
-    float mu = rb == 0 ? m_ref0 : m_ref1;
-    mu = mu == -INFINITY ? 0.f : -mu;
+    // ---- probabilities of this wavefront's 32 keys x 32 rows, optimistically
+    // against the current reference max: exp2(s * scale2 - m_ref), one fma
+    // each (exp2(-inf) = 0 for masked keys). Only if some row of some
+    // wavefront outgrew its reference by more than 2^8 (always on a split's
+    // first visible tile) do all four take the exchange-and-rescale path
+    // below and recompute; they all read the same flags, so they agree.
     bf16x8_t pf[2];
     float pj[16];
+    auto probabilities = [&]() -> float {
+      float mu = rb == 0 ? m_ref0 : m_ref1;
+      mu = mu == -INFINITY ? 0.f : -mu;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      pj[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[j], scale2, mu));
-      pf[j >> 3][j & 7] = (__bf16)pj[j];
-    }
-    l_part += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7])) +
-              (((pj[8] + pj[9]) + (pj[10] + pj[11])) + ((pj[12] + pj[13]) + (pj[14] + pj[15])));
-    pex[(wave * 2 + 0) * 64 + lane] = as_u4(pf[0]);
-    pex[(wave * 2 + 1) * 64 + lane] = as_u4(pf[1]);
+      for (int j = 0; j < 16; ++j) {
+        pj[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[j], scale2, mu));
+        pf[j >> 3][j & 7] = (__bf16)pj[j];
+      }
+      pex[(wave * 2 + 0) * 64 + lane] = as_u4(pf[0]);
+      pex[(wave * 2 + 1) * 64 + lane] = as_u4(pf[1]);
+      return ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7])) +
+             (((pj[8] + pj[9]) + (pj[10] + pj[11])) + ((pj[12] + pj[13]) + (pj[14] + pj[15])));
+    };
+    const bool outgrown = __ballot(tm > (rb == 0 ? m_ref0 : m_ref1) + kRescaleLog2) != 0;
+    float psum = probabilities();
+    if (hf == 0) mex[wave * 32 + col] = tm;
+    if (lane == 0) rescale_flag[wave] = outgrown;
     lds_barrier();
 
-    // ---- O^T += V^T P^T for latent entries [128 wave, +128), both row blocks.
-    // Output register j of the score MFMA in lane half hf holds key
-    // 8(j/4) + 4hf + j%4 of its 32; k-step c of the value product takes
-    // registers 8c..8c+7, i.e. keys 16c + 8(j'/4) + 4hf + j'%4, j' = 0..7.
-    // The transposed reads fetch V rows base..base+3 and base+8..base+11.
-    // Four operand groups g = (kh2, c): eight transposed V^T reads (four
-    // 32-entry blocks x two key quads) and the two P^T operands (one per row
-    // block). Group g+1's reads are issued before group g's eight MFMAs.
-    i16x4_t loA[4], hiA[4], loB[4], hiB[4];
-    u32x4_t pbA[2], pbB[2];
-    auto issue = [&](int grp, i16x4_t* lo, i16x4_t* hi, u32x4_t* pb) {
-      const int kh2 = grp >> 1, c = grp & 1;
-      const char* vb = cur + (32 * kh2 + 16 * c) * kLatRow + L.vbase;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        lo[db] = tr_read(vb + ((L.vt ^ (4 * db)) << 4));
-        hi[db] = tr_read(vb + 8 * kLatRow + ((L.vt ^ (4 * db) ^ 8) << 4));
-      }
-#pragma unroll
-      for (int x = 0; x < 2; ++x) pb[x] = lds_read128(&pex[((x + 2 * kh2) * 2 + c) * 64 + ln]);
-    };
-    auto product = [&](const i16x4_t* lo, const i16x4_t* hi, const u32x4_t* pb) {
-      bf16x8_t va[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) va[db] = cat4(lo[db], hi[db]);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const bf16x8_t pbx = __builtin_bit_cast(bf16x8_t, pb[x]);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[x][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pbx, o[x][db], 0, 0, 0);
-      }
-    };
+    // The flags are read along with group 0's operands. If any is set, all
+    // four wavefronts exchange maxima, rescale, recompute and re-share their
+    // probabilities, and re-read group 0 (its P^T operands were stale).
+    u32x4_t fl = lds_read128(rescale_flag);
+    issue_p(0, pbA);
+    TVMLA_LDS_WAIT_F(loA, hiA, pbA, fl);
+    if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3])) {
+      // Every wavefront sees the same maxima and the same m_ref, so all four
+      // rescale alike and keep identical references.
+      const float tm0 = fmaxf(mex[col], mex[64 + col]);       // row block 0: wavefronts 0, 2
+      const float tm1 = fmaxf(mex[32 + col], mex[96 + col]);  // row block 1: wavefronts 1, 3
+      rescale(o[0], m_ref0, rb == 0, tm0);
+      rescale(o[1], m_ref1, rb == 1, tm1);
+      psum = probabilities();
+      lds_barrier();
+      issue(0, loA, hiA, pbA);
+      TVMLA_LDS_WAIT(loA, hiA, pbA);
+    }
+    l_part += psum;
     // The scheduling barriers keep each group's MFMAs between the waits
     // (the compiler may otherwise hoist the next wait above them).
-    issue(0, loA, hiA, pbA);
-    TVMLA_LDS_WAIT(loA, hiA, pbA);
     issue(1, loB, hiB, pbB);
     TVMLA_PIN(loA, hiA, pbA);
     product(loA, hiA, pbA);
