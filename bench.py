@@ -101,10 +101,11 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="long185k")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
     ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--nsplit", type=int, default=0, help="override the workload's split count (diagnostics)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the verify step, time a plain device copy of this many MiB "
@@ -113,7 +114,7 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verify path shards by heads or requests with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the verify path shards by heads or requests with no exchange)", file=sys.stderr)
         return 2
 
     import torch
@@ -142,7 +143,7 @@ def main(argv=None):
         ms = e0.elapsed_time(e1) / args.steps
         print(json.dumps({"copy_bytes": n, "ms": ms, "read_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return 0
-    w = gen.build(args.workload)
+    w = gen.build(args.workload, **({"nsplit": args.nsplit} if args.nsplit else {}))
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
     pool = w.device_pool(dev, fill=0.0)
     kv = pool
@@ -176,6 +177,16 @@ def main(argv=None):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / k  # ms
 
+    # Power-state settle (untimed): the GPU reaches steady clocks only after
+    # some tens of milliseconds of load, and calls made before that run up to
+    # ~15% slower. Serving runs at steady clocks, so before the warm-up steps
+    # the step runs in batches of 10 until 150 ms of load have passed.
+    settle_calls, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < 0.15:
+        for _ in range(10):
+            step()
+        settle_calls += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -207,6 +218,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_calls": settle_calls,
         "ms_per_step": round(ms_step, 5),
         "us_per_call": round(ms_step * 1e3, 2),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 5),
