@@ -63,12 +63,14 @@ constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over 
 constexpr float kRescaleLog2 = 8.f;                    // lazy-rescale threshold (log2 units)
 constexpr int kRing = 6;                               // score operand reads in flight per wavefront
 
-// Piece swizzle of key k: a permutation of 0..15 over 16 consecutive keys
-// (the 16 lanes an LDS read cycle serves for the score operand) whose bits
-// 1..3 also differ across 4 consecutive keys (the 4 rows a transposed read
-// of 16 lanes covers, two adjacent pieces each). Latent pieces XOR all four
-// bits (staying inside their aligned group of 16), rope pieces the low three.
-__device__ __forceinline__ int piece_swz(int k) { return ((k >> 2) & 1) | ((k & 3) << 1) | (k & 8); }
+// Piece swizzle of key k (LDS serves 256 bytes = 16 pieces per cycle): the
+// low two key bits go to piece bits 2..3 and key bits 2..3 to piece bits
+// 0..1. Over 16 consecutive keys (the 16 lanes of one score-operand read
+// cycle) it is a permutation of 0..15, and for the 4 consecutive keys x 4
+// adjacent pieces a cycle of transposed reads covers it yields 16 distinct
+// slots. Latent pieces XOR it (staying inside their aligned group of 16).
+__host__ __device__ constexpr int piece_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+constexpr int kSwzHi = piece_swz(8) ^ piece_swz(0);  // swz(k + 8) ^ swz(k) for k % 16 < 8
 
 // Workgroup barrier for LDS exchanges: waits only for this wavefront's LDS
 // operations (lgkmcnt), not for its global loads -- the next tile's
@@ -444,7 +446,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         lo[db] = tr_read(vb + ((L.vt ^ (4 * db)) << 4));
-        hi[db] = tr_read(vb + 8 * kLatRow + ((L.vt ^ (4 * db) ^ 8) << 4));
+        hi[db] = tr_read(vb + 8 * kLatRow + ((L.vt ^ (4 * db) ^ kSwzHi) << 4));
       }
     };
     auto issue_p = [&](int grp, u32x4_t* pb) {
