@@ -9,8 +9,14 @@
 // not read, so the workspace needs no clearing between calls; a split that
 // held keys but saw none of them wrote lse_s = -inf and weighs nothing.
 //
-// One 64-lane wavefront per output row; lane l owns entries [8l, 8l+8).
-// The partial rows are read as 2 KB contiguous segments (HBM-bound).
+// W wavefronts per output row, W in {1, 4, 16}, chosen from the row count so
+// that a launch has enough wavefronts in flight to keep HBM busy. The row's
+// split maximum and weight sum are reductions over the lse_s (one split per
+// lane of the row's wavefronts); wavefront w of the row then accumulates the
+// weighted partial rows of splits s = w, w+W, w+2W, ... (lane l owns entries
+// [8l, 8l+8); four or eight 2 KB rows in flight per wavefront), and for W > 1 the
+// accumulators are added through LDS. Reads are contiguous 2 KB segments
+// (HBM-bound).
 
 #include "tvmla_internal.h"
 
@@ -29,13 +35,20 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
+
+// W wavefronts per row; a workgroup holds kRowsWG = max(1, 4 / W) rows.
+template <bool kBf16, int W>
+__global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombineParams c) {
+  constexpr int kRowsWG = W >= 4 ? 1 : 4 / W;
+  constexpr int kUnroll = W == 1 ? 4 : 8;  // partial rows in flight per wavefront
+  __shared__ float red_m[kRowsWG * W], red_l[kRowsWG * W];
+  __shared__ __attribute__((aligned(16))) float red_o[W > 1 ? W - 1 : 1][kDLatent];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int wr = wave % W;  // wavefront within its row
   const int R = c.num_draft * c.num_heads;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= (int64_t)c.batch * R) return;
+  const int64_t row = (int64_t)blockIdx.x * kRowsWG + wave / W;
+  if (row >= (int64_t)c.batch * R) return;  // only with W = 1; no barrier follows then
   const int b = (int)(row / R);
   const int r = (int)(row - (int64_t)b * R);
 
@@ -46,28 +59,63 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
   }
   const size_t base = (size_t)b * c.nsplit * R + r;  // partial row of split 0
 
+  // M = max_s lse_s over the row's wavefronts
   float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, c.lse_part[base + (size_t)s * R]);
+  for (int s = wr * 64 + lane; s < ns; s += 64 * W) mx = fmaxf(mx, c.lse_part[base + (size_t)s * R]);
   mx = wave_max(mx);
+  if (W > 1) {
+    if (lane == 0) red_m[wave] = mx;
+    __syncthreads();
+    mx = red_m[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, red_m[w]);
+  }
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    for (int s = lane; s < ns; s += 64) wsum += exp2f((c.lse_part[base + (size_t)s * R] - mx) * kLog2e);
+    for (int s = wr * 64 + lane; s < ns; s += 64 * W) wsum += exp2f((c.lse_part[base + (size_t)s * R] - mx) * kLog2e);
     wsum = wave_sum(wsum);
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
+    auto add = [&](int s) {
       const size_t pr = base + (size_t)s * R;
       const float w = exp2f((c.lse_part[pr] - mx) * kLog2e);
       const float4* src = reinterpret_cast<const float4*>(c.o_part + pr * kDLatent + 8 * lane);
       const float4 a = src[0], d = src[1];
-      if (w > 0.f) {
+      if (w > 0.f) {  // a split whose row saw no visible key (lse_s = -inf) weighs nothing
         acc[0] = fmaf(w, a.x, acc[0]); acc[1] = fmaf(w, a.y, acc[1]);
         acc[2] = fmaf(w, a.z, acc[2]); acc[3] = fmaf(w, a.w, acc[3]);
         acc[4] = fmaf(w, d.x, acc[4]); acc[5] = fmaf(w, d.y, acc[5]);
         acc[6] = fmaf(w, d.z, acc[6]); acc[7] = fmaf(w, d.w, acc[7]);
       }
+    };
+    int s = wr;
+    for (; s + W * (kUnroll - 1) < ns; s += W * kUnroll) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) add(s + W * u);
     }
+    for (; s < ns; s += W) add(s);
+  }
+  if (W > 1) {
+    if (lane == 0) red_l[wave] = wsum;
+    if (wr > 0) {
+      float4* dst = reinterpret_cast<float4*>(&red_o[wr - 1][8 * lane]);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wr != 0) return;
+    wsum = red_l[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) wsum += red_l[w];
+#pragma unroll
+    for (int w = 0; w < W - 1; ++w) {
+      const float4* src = reinterpret_cast<const float4*>(&red_o[w][8 * lane]);
+      const float4 a = src[0], d = src[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += d.x; acc[5] += d.y; acc[6] += d.z; acc[7] += d.w;
+    }
+  }
+  if (mx != -INFINITY) {
     const float inv = 1.f / wsum;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
@@ -89,16 +137,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
   if (lane == 0) c.lse[row] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
 }
 
+template <int W>
+hipError_t launch_w(const CombineParams& c, int dtype, int64_t rows, hipStream_t stream) {
+  constexpr int kRowsWG = W >= 4 ? 1 : 4 / W;
+  dim3 grid((unsigned)((rows + kRowsWG - 1) / kRowsWG));
+  CombineParams arg = c;
+  void* args[] = {&arg};
+  const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&combine_kernel<true, W>)
+                              : reinterpret_cast<const void*>(&combine_kernel<false, W>);
+  return hipLaunchKernel(fn, grid, dim3(W == 16 ? 1024 : 256), args, 0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& c, int dtype, hipStream_t stream) {
+  // enough wavefronts for HBM: ~4096 rows and up take one each, fewer rows more
   const int64_t rows = (int64_t)c.batch * c.num_draft * c.num_heads;
-  dim3 grid((unsigned)((rows + 3) / 4));
-  CombineParams arg = c;
-  void* args[] = {&arg};
-  const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&combine_kernel<true>)
-                              : reinterpret_cast<const void*>(&combine_kernel<false>);
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
+  if (rows >= 4096) return launch_w<1>(c, dtype, rows, stream);
+  if (rows >= 512) return launch_w<4>(c, dtype, rows, stream);
+  return launch_w<16>(c, dtype, rows, stream);
 }
 
 }  // namespace tvmla
