@@ -188,6 +188,37 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
                            int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit,
                            int32_t min_chunk, int32_t dtype, void* out, float* lse, void* stream);
 
+/*
+ * KV defragmentation: copy every request's prefix rows into one contiguous
+ * run of cache slots and rewrite its indices. page_size = 1 paging scatters
+ * a request's rows over the pool, so every read of them gathers isolated
+ * rows ("The Plan Document: A Pivot Point in Custom CUDA Kernel
+ * Development", section "Context: The Bottleneck That Demanded a Custom
+ * Kernel"); compaction is the plan's last phase (same page, section "Output
+ * Knowledge Created"). The interface is this library's own reading:
+ *
+ *   for b < batch, p < P_b = kv_indptr[b+1] - kv_indptr[b]:
+ *     kv_dst[dst_base[b] + p][0:576] = kv_src[kv_indices[kv_indptr[b] + p]][0:576]
+ *     kv_indices_out[kv_indptr[b] + p] = dst_base[b] + p
+ *
+ * kv_src, kv_dst   caches of `dtype` (rows of src_stride_row / dst_stride_row
+ *                  elements, >= 576; entries past 576 are not touched). They
+ *                  may be the same cache.
+ * kv_indptr, kv_indices   as for tvmla_verify (read only).
+ * dst_base         int32 [batch]: first destination slot of each request.
+ * kv_indices_out   int32 [kv_indptr[batch]]: the rewritten indices; may be
+ *                  kv_indices itself (the index rewrite is enqueued after
+ *                  the copy).
+ * Draft rows (out_cache_loc) are not moved. The destination runs must not
+ * overlap each other or any source row of the same call (the caller picks
+ * free slots); overlapping runs are undefined behaviour.
+ * Alignment: caches 16-byte aligned, row strides multiples of 16 bytes.
+ * Limits: 1 <= batch <= 65535. Enqueues two kernels on `stream`.
+ */
+tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_dst, int64_t dst_stride_row,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* dst_base,
+                          int32_t* kv_indices_out, int32_t batch, int32_t dtype, void* stream);
+
 /* A static, human-readable name for a status code (host pointer, never NULL). */
 const char* tvmla_status_str(int32_t status);
 

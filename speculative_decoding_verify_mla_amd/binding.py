@@ -32,7 +32,7 @@ STATUS = {
 
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_partials",
-           "tvmla_combine", "tvmla_status_str", "tvmla_version")
+           "tvmla_combine", "tvmla_defrag", "tvmla_status_str", "tvmla_version")
 
 
 class TvmlaError(RuntimeError):
@@ -68,6 +68,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_verify_partials.restype = ctypes.c_int
     lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
     lib.tvmla_combine.restype = ctypes.c_int
+    lib.tvmla_defrag.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I32, _I32, _P]
+    lib.tvmla_defrag.restype = ctypes.c_int
     lib.tvmla_status_str.argtypes = [_I32]
     lib.tvmla_status_str.restype = ctypes.c_char_p
     lib.tvmla_version.argtypes = []
@@ -193,3 +195,18 @@ def workspace_views(workspace, batch: int, num_draft: int, num_heads: int, nspli
     o = raw[:o_bytes].view(torch.float32).view(batch, nsplit, R, D_LATENT)
     lse = raw[lse_off:lse_off + rows * 4].view(torch.float32).view(batch, nsplit, R)
     return o, lse
+
+
+def defrag(kv_src, kv_dst, kv_indptr, kv_indices, dst_base, kv_indices_out, stream=None) -> None:
+    """Enqueue tvmla_defrag: move each request's prefix rows of kv_src to slots
+    dst_base[b] + p of kv_dst and write the new indices to kv_indices_out
+    (which may be kv_indices itself)."""
+    if kv_src.dtype != kv_dst.dtype:
+        raise TvmlaError(3, "kv_src and kv_dst must share one dtype")
+    if kv_src.stride(1) != 1 or kv_dst.stride(1) != 1:
+        raise TvmlaError(5, "cache rows must be contiguous")
+    batch = kv_indptr.numel() - 1
+    st = load().tvmla_defrag(_ptr(kv_src), kv_src.stride(0), _ptr(kv_dst), kv_dst.stride(0), _ptr(kv_indptr),
+                             _ptr(kv_indices), _ptr(dst_base), _ptr(kv_indices_out), batch,
+                             _dtype_code(kv_src), _stream_ptr(stream))
+    _check(st)

@@ -210,4 +210,28 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
   return TVMLA_OK;
 }
 
+tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_dst, int64_t dst_stride_row,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* dst_base,
+                          int32_t* kv_indices_out, int32_t batch, int32_t dtype, void* stream) {
+  if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
+  if (!kv_src || !kv_dst || !kv_indptr || !kv_indices || !dst_base || !kv_indices_out) return TVMLA_E_NULLPTR;
+  if (batch < 1 || batch > 65535) return TVMLA_E_SHAPE;
+  if (src_stride_row < TVMLA_D_KEY || dst_stride_row < TVMLA_D_KEY) return TVMLA_E_SHAPE;
+  const int64_t esz = dtype == TVMLA_BF16 ? 2 : 4;
+  if (!aligned16(kv_src) || !aligned16(kv_dst) || (src_stride_row * esz) % 16 || (dst_stride_row * esz) % 16)
+    return TVMLA_E_ALIGN;
+  DefragParams d;
+  d.src = kv_src;
+  d.dst = kv_dst;
+  d.src_row_bytes = src_stride_row * esz;
+  d.dst_row_bytes = dst_stride_row * esz;
+  d.kv_indptr = kv_indptr;
+  d.kv_indices = kv_indices;
+  d.dst_base = dst_base;
+  d.indices_out = kv_indices_out;
+  d.batch = batch;
+  if (launch_defrag(d, (int)esz, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
 }  // extern "C"

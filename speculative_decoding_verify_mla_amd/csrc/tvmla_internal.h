@@ -41,6 +41,17 @@ struct CombineParams {
   float* lse;
 };
 
+struct DefragParams {
+  const void* src;
+  void* dst;
+  int64_t src_row_bytes, dst_row_bytes;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* dst_base;
+  int32_t* indices_out;
+  int32_t batch;
+};
+
 // Workspace regions (byte offsets from the workspace base).
 struct WorkspaceLayout {
   size_t o_off, lse_off, total;
@@ -92,5 +103,6 @@ hipError_t launch_split_scalar_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_scalar_fp32(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_mfma_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& c, int dtype, hipStream_t stream);
+hipError_t launch_defrag(const DefragParams& d, int elem_size, hipStream_t stream);
 
 }  // namespace tvmla

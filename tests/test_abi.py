@@ -152,3 +152,32 @@ def test_partials_errors(lib):
         a = list(good)
         a[idx] = val
         assert f(*a) == code, (idx, val)
+
+
+def _defrag(lib, **kw):
+    a = dict(src=_FAKE, src_stride=576, dst=_FAKE, dst_stride=576, indptr=_FAKE, indices=_FAKE, base=_FAKE,
+             out=_FAKE, batch=2, dtype=binding.BF16, stream=None)
+    a.update(kw)
+    return lib.tvmla_defrag(a["src"], a["src_stride"], a["dst"], a["dst_stride"], a["indptr"], a["indices"],
+                            a["base"], a["out"], a["batch"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("field", ["src", "dst", "indptr", "indices", "base", "out"])
+def test_defrag_null_pointer(lib, field):
+    assert _defrag(lib, **{field: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(batch=65536), dict(src_stride=575), dict(dst_stride=100)])
+def test_defrag_bad_shape(lib, kw):
+    assert _defrag(lib, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1)])
+def test_defrag_bad_dtype(lib, kw):
+    assert _defrag(lib, **kw) == 3
+
+
+@pytest.mark.parametrize("kw", [dict(src=_FAKE + 8), dict(dst=_FAKE + 4), dict(src_stride=580),
+                                dict(dst_stride=578, dtype=binding.FP32)])
+def test_defrag_misaligned(lib, kw):
+    assert _defrag(lib, **kw) == 5
