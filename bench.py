@@ -97,6 +97,72 @@ def cpu_baseline(w, pool_host):
     }
 
 
+def bench_defrag(args, w, torch, binding):
+    """tvmla_defrag on the workload: every prefix moves to a fresh contiguous
+    run appended to the cache (indices written to a separate array, so each
+    timed call does the same work). HBM-bound: per moved row 2 x 576 x
+    elem_size bytes plus 8 bytes of indices. Also times the verify step on
+    the scattered and on the compacted layout (the read-side gain)."""
+    import numpy as np
+
+    dev = "cuda"
+    pool = w.device_pool(dev, fill=0.0)
+    P = np.diff(w.kv_indptr.numpy())
+    n = int(P.sum())
+    first = pool.shape[0]
+    pool = torch.cat([pool, torch.zeros((n, pool.shape[1]), dtype=pool.dtype, device=dev)], 0)
+    bases = torch.from_numpy((first + np.concatenate([[0], np.cumsum(P)[:-1]])).astype(np.int32)).to(dev)
+    indptr, idx = w.kv_indptr.to(dev), w.kv_indices.to(dev)
+    new_idx = torch.empty_like(idx)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    def defrag():
+        binding.defrag(pool, pool, indptr, idx, bases, new_idx, stream=stream)
+
+    T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
+    q_nope, q_rope = w.q_nope.to(dev), w.q_rope.to(dev)
+    ocl, mask, mask_indptr = w.out_cache_loc.to(dev), w.custom_mask.to(dev), w.mask_indptr.to(dev)
+    out = torch.empty((w.batch * T, H, 512), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((w.batch * T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.workspace_bytes(w.batch, T, H, ns), dtype=torch.uint8, device=dev)
+
+    def verify_with(indices):
+        return lambda: binding.verify(q_nope, q_rope, pool, indptr, indices, ocl, mask, mask_indptr, w.sm_scale,
+                                      ns, out, lse, ws, T, stream=stream)
+
+    for _ in range(max(args.warmup, 20)):
+        defrag()
+    ms_defrag = timed(defrag, args.steps)
+    for _ in range(max(args.warmup, 20)):
+        verify_with(idx)()
+    ms_scattered = timed(verify_with(idx), args.steps)
+    ms_compact = timed(verify_with(new_idx), args.steps)
+    esz = pool.element_size()
+    moved = n * (2 * 576 * esz + 8)
+    gbs = moved / (ms_defrag * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "tvmla_defrag GB/s moved (HBM roofline) and verify step before/after compaction",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "us_per_defrag": round(ms_defrag * 1e3, 2), "rows_moved": n, "bytes_moved": moved,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "verify_us": {"scattered": round(ms_scattered * 1e3, 2), "compacted": round(ms_compact * 1e3, 2)},
+        "config": {"workload": args.workload, "batch": w.batch, "num_draft": T, "num_heads": H, "nsplit": ns},
+        "dtype": w.spec.dtype, "data": "synthetic",
+    }), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +172,9 @@ def main(argv=None):
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--nsplit", type=int, default=0, help="override the workload's split count (diagnostics)")
+    ap.add_argument("--op", default="verify", choices=["verify", "defrag"],
+                    help="defrag: time tvmla_defrag on the workload (a separate diagnostic line, not the "
+                         "verify bench line) and the verify step before and after compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the verify step, time a plain device copy of this many MiB "
@@ -144,6 +213,8 @@ def main(argv=None):
         print(json.dumps({"copy_bytes": n, "ms": ms, "read_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return 0
     w = gen.build(args.workload, **({"nsplit": args.nsplit} if args.nsplit else {}))
+    if args.op == "defrag":
+        return bench_defrag(args, w, torch, binding)
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
     pool = w.device_pool(dev, fill=0.0)
     kv = pool
