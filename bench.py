@@ -163,6 +163,45 @@ def bench_defrag(args, w, torch, binding):
     return 0
 
 
+def bench_tree_mask(args, w, torch, binding):
+    """tvmla_tree_mask on the workload's trees: T * N_b mask bytes written per
+    request (HBM-bound when large, launch-bound when small)."""
+    import numpy as np
+
+    dev = "cuda"
+    T = w.num_draft
+    parents = torch.from_numpy(np.concatenate(w.parents).astype(np.int32)).to(dev)
+    indptr = w.kv_indptr.to(dev)
+    mask = torch.empty_like(w.custom_mask, device=dev)
+    mindptr = torch.empty_like(w.mask_indptr, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        binding.tree_mask(parents, indptr, T, mask, mindptr, stream=stream)
+
+    for _ in range(max(args.warmup, 20)):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = mask.numel() + 4 * (mindptr.numel() + indptr.numel() + parents.numel())
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "tvmla_tree_mask us per call (mask bytes written, HBM roofline)",
+        "value": round(ms * 1e3, 2), "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+        "mask_bytes": mask.numel(),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "config": {"workload": args.workload, "batch": w.batch, "num_draft": T}, "data": "synthetic",
+    }), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,7 +211,7 @@ def main(argv=None):
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--nsplit", type=int, default=0, help="override the workload's split count (diagnostics)")
-    ap.add_argument("--op", default="verify", choices=["verify", "defrag"],
+    ap.add_argument("--op", default="verify", choices=["verify", "defrag", "tree_mask"],
                     help="defrag: time tvmla_defrag on the workload (a separate diagnostic line, not the "
                          "verify bench line) and the verify step before and after compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,6 +254,8 @@ def main(argv=None):
     w = gen.build(args.workload, **({"nsplit": args.nsplit} if args.nsplit else {}))
     if args.op == "defrag":
         return bench_defrag(args, w, torch, binding)
+    if args.op == "tree_mask":
+        return bench_tree_mask(args, w, torch, binding)
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
     pool = w.device_pool(dev, fill=0.0)
     kv = pool

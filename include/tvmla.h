@@ -219,6 +219,31 @@ tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_d
                           const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* dst_base,
                           int32_t* kv_indices_out, int32_t batch, int32_t dtype, void* stream);
 
+/*
+ * Visibility mask of the draft trees, built on the device (no host
+ * marshaling; capture-safe). A DDTree drafter proposes a tree of draft tokens
+ * verified in one pass, which needs a mask of which draft token sees which
+ * key ("The Architecture of Capture Safety: Designing a CUDA
+ * Graph-Compatible Verify Kernel for SGLang", section "Input Knowledge
+ * Required", DDTree paragraph); this writes it in the raw custom_mask +
+ * mask_indptr form tvmla_verify reads (same page, section "The Design
+ * Emerges", third insight).
+ *
+ * parents      int32 [batch * num_draft]: parents[b*T + i] is the parent of
+ *              draft node i of request b (-1 for the root, node 0); a parent
+ *              precedes its child (parents[b*T + i] < i). A parent that does
+ *              not precede its child ends the walk there (no hang).
+ * kv_indptr    int32 [batch+1], as for tvmla_verify (P_b prefix keys).
+ * custom_mask  uint8 output, sum_b T * (P_b + T) bytes: row i of request b
+ *              is 1 on every prefix column and on draft column P_b + j iff j
+ *              is i or an ancestor of i, 0 elsewhere.
+ * mask_indptr  int32 [batch+1] output: mask_indptr[b] = T*(kv_indptr[b] -
+ *              kv_indptr[0]) + T*T*b; the total must stay below 2^31.
+ * Limits: 1 <= batch <= 65535; 1 <= num_draft <= 64. One kernel on `stream`.
+ */
+tvmla_status tvmla_tree_mask(const int32_t* parents, const int32_t* kv_indptr, int32_t batch, int32_t num_draft,
+                             uint8_t* custom_mask, int32_t* mask_indptr, void* stream);
+
 /* A static, human-readable name for a status code (host pointer, never NULL). */
 const char* tvmla_status_str(int32_t status);
 

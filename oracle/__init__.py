@@ -9,5 +9,6 @@ verify_fp64  vectorised fp64 definition (NumPy), split partials and the
              log-sum-exp combine
 brute        pure-Python scalar loops with math.fsum, used to pin verify_fp64
 defrag       compaction of a request's prefix rows into a contiguous run
+tree_mask    the visibility mask built from draft-tree parent arrays
 """
-from . import brute, defrag, verify_fp64  # noqa: F401
+from . import brute, defrag, tree_mask, verify_fp64  # noqa: F401

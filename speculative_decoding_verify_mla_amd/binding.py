@@ -32,7 +32,7 @@ STATUS = {
 
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_partials",
-           "tvmla_combine", "tvmla_defrag", "tvmla_status_str", "tvmla_version")
+           "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version")
 
 
 class TvmlaError(RuntimeError):
@@ -70,6 +70,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_combine.restype = ctypes.c_int
     lib.tvmla_defrag.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I32, _I32, _P]
     lib.tvmla_defrag.restype = ctypes.c_int
+    lib.tvmla_tree_mask.argtypes = [_P, _P, _I32, _I32, _P, _P, _P]
+    lib.tvmla_tree_mask.restype = ctypes.c_int
     lib.tvmla_status_str.argtypes = [_I32]
     lib.tvmla_status_str.restype = ctypes.c_char_p
     lib.tvmla_version.argtypes = []
@@ -209,4 +211,13 @@ def defrag(kv_src, kv_dst, kv_indptr, kv_indices, dst_base, kv_indices_out, stre
     st = load().tvmla_defrag(_ptr(kv_src), kv_src.stride(0), _ptr(kv_dst), kv_dst.stride(0), _ptr(kv_indptr),
                              _ptr(kv_indices), _ptr(dst_base), _ptr(kv_indices_out), batch,
                              _dtype_code(kv_src), _stream_ptr(stream))
+    _check(st)
+
+
+def tree_mask(parents, kv_indptr, num_draft: int, custom_mask, mask_indptr, stream=None) -> None:
+    """Enqueue tvmla_tree_mask: build custom_mask / mask_indptr on the device
+    from int32 parents [batch*num_draft] (-1 for each root)."""
+    batch = kv_indptr.numel() - 1
+    st = load().tvmla_tree_mask(_ptr(parents), _ptr(kv_indptr), batch, num_draft, _ptr(custom_mask),
+                                _ptr(mask_indptr), _stream_ptr(stream))
     _check(st)

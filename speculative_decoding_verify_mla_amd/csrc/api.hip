@@ -234,4 +234,20 @@ tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_d
   return TVMLA_OK;
 }
 
+tvmla_status tvmla_tree_mask(const int32_t* parents, const int32_t* kv_indptr, int32_t batch, int32_t num_draft,
+                             uint8_t* custom_mask, int32_t* mask_indptr, void* stream) {
+  if (!parents || !kv_indptr || !custom_mask || !mask_indptr) return TVMLA_E_NULLPTR;
+  if (batch < 1 || batch > 65535) return TVMLA_E_SHAPE;
+  if (num_draft < 1 || num_draft > TVMLA_MAX_DRAFT) return TVMLA_E_SHAPE;
+  TreeMaskParams m;
+  m.parents = parents;
+  m.kv_indptr = kv_indptr;
+  m.mask = custom_mask;
+  m.mask_indptr = mask_indptr;
+  m.batch = batch;
+  m.num_draft = num_draft;
+  if (launch_tree_mask(m, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
 }  // extern "C"

@@ -52,6 +52,14 @@ struct DefragParams {
   int32_t batch;
 };
 
+struct TreeMaskParams {
+  const int32_t* parents;    // [batch * num_draft], parent of node i within its request, -1 for the root
+  const int32_t* kv_indptr;  // [batch + 1]
+  uint8_t* mask;
+  int32_t* mask_indptr;      // [batch + 1]
+  int32_t batch, num_draft;
+};
+
 // Workspace regions (byte offsets from the workspace base).
 struct WorkspaceLayout {
   size_t o_off, lse_off, total;
@@ -104,5 +112,6 @@ hipError_t launch_split_scalar_fp32(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_mfma_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& c, int dtype, hipStream_t stream);
 hipError_t launch_defrag(const DefragParams& d, int elem_size, hipStream_t stream);
+hipError_t launch_tree_mask(const TreeMaskParams& m, hipStream_t stream);
 
 }  // namespace tvmla

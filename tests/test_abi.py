@@ -181,3 +181,20 @@ def test_defrag_bad_dtype(lib, kw):
                                 dict(dst_stride=578, dtype=binding.FP32)])
 def test_defrag_misaligned(lib, kw):
     assert _defrag(lib, **kw) == 5
+
+
+def _tree_mask(lib, **kw):
+    a = dict(parents=_FAKE, indptr=_FAKE, batch=2, T=9, mask=_FAKE, mask_indptr=_FAKE, stream=None)
+    a.update(kw)
+    return lib.tvmla_tree_mask(a["parents"], a["indptr"], a["batch"], a["T"], a["mask"], a["mask_indptr"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("field", ["parents", "indptr", "mask", "mask_indptr"])
+def test_tree_mask_null_pointer(lib, field):
+    assert _tree_mask(lib, **{field: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(batch=65536), dict(T=0), dict(T=65)])
+def test_tree_mask_bad_shape(lib, kw):
+    assert _tree_mask(lib, **kw) == 2
