@@ -154,6 +154,34 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
                              size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
 
 /*
+ * tvmla_verify_ex for draft trees of different sizes per request: request b
+ * has T_b = qo_indptr[b+1] - qo_indptr[b] draft tokens, query rows
+ * qo_indptr[b] .. qo_indptr[b+1]-1 (the int64 token offsets named on "The
+ * Architecture of Capture Safety: ...", section "Input Knowledge Required";
+ * the ragged layout is this library's reading). Everything else is as for
+ * tvmla_verify_ex with num_draft replaced by max_draft = the largest T_b:
+ *   - N_b = P_b + T_b keys: the prefix, then out_cache_loc[qo_indptr[b] ..
+ *     qo_indptr[b+1]-1];
+ *   - custom_mask: per request a row-major [T_b][N_b] block at
+ *     mask_indptr[b];
+ *   - q_nope/q_rope/out/lse: qo_indptr[batch] token rows in all;
+ *   - workspace: tvmla_workspace_bytes(batch, max_draft, num_heads, nsplit);
+ *   - the launch depends only on the scalars (max_draft fixes the grid;
+ *     row groups past a request's T_b return at once), so token counts may
+ *     change between graph replays.
+ * qo_indptr (int64 [batch+1], device) must be non-decreasing; a T_b above
+ * max_draft is clamped to max_draft (the request's last tokens are ignored).
+ */
+tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                 const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                 const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                 const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
+                                 int32_t batch, int32_t max_draft, int32_t num_heads, float sm_scale,
+                                 int32_t nsplit, int32_t dtype, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
+
+/*
  * The split step alone: the same arguments as tvmla_verify_ex without out
  * and lse. It enqueues only the split kernel, which leaves every non-empty
  * split's partial result in the workspace (layout under

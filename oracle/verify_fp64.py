@@ -148,6 +148,38 @@ def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custo
     return out, lse
 
 
+def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask,
+                  mask_indptr, qo_indptr, sm_scale: float):
+    """Oracle for draft trees of different sizes: request b owns query tokens
+    qo_indptr[b] .. qo_indptr[b+1]-1 (T_b of them; the int64 token offsets of
+    page 1, "Input Knowledge Required"), its draft keys are out_cache_loc at
+    the same positions, its mask block is [T_b][P_b + T_b] at mask_indptr[b].
+    Returns out [qo_indptr[-1], H, 512] and lse [qo_indptr[-1], H], fp64."""
+    qn_all = _f64(q_nope)
+    qr_all = _f64(q_rope)
+    qo = _i64(qo_indptr)
+    ip = _i64(kv_indptr)
+    ocl = _i64(out_cache_loc)
+    H = qn_all.shape[1]
+    ntok = int(qo[-1])
+    out = np.zeros((ntok, H, D_LATENT))
+    lse = np.zeros((ntok, H))
+    for b in range(len(qo) - 1):
+        t0, t1 = int(qo[b]), int(qo[b + 1])
+        Tb = t1 - t0
+        if Tb == 0:
+            continue
+        slots = np.concatenate([_i64(kv_indices)[ip[b]:ip[b + 1]], ocl[t0:t1]])
+        keys = request_keys(kv_cache, slots)
+        vis = visibility(custom_mask, mask_indptr, b, Tb, len(slots))
+        qn = qn_all[t0:t1].reshape(Tb * H, D_LATENT)
+        qr = qr_all[t0:t1].reshape(Tb * H, D_ROPE)
+        o, ls = attend(qn, qr, keys, np.repeat(vis, H, axis=0), sm_scale)
+        out[t0:t1] = o.reshape(Tb, H, D_LATENT)
+        lse[t0:t1] = ls.reshape(Tb, H)
+    return out, lse
+
+
 def verify_rows(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask,
                 mask_indptr, sm_scale: float, num_draft: int, picks):
     """Oracle for selected (token, head) pairs only, for spot checks at full size.

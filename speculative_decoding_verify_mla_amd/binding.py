@@ -31,7 +31,7 @@ STATUS = {
 }
 
 # every symbol include/tvmla.h declares
-EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_partials",
+EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_ragged", "tvmla_verify_partials",
            "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version")
 
 
@@ -64,6 +64,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_verify.restype = ctypes.c_int
     lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32]
     lib.tvmla_verify_ex.restype = ctypes.c_int
+    lib.tvmla_verify_ragged.argtypes = _VERIFY_ARGS[:13] + [_P] + _VERIFY_ARGS[13:] + [_I32, _I32]
+    lib.tvmla_verify_ragged.restype = ctypes.c_int
     lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32]
     lib.tvmla_verify_partials.restype = ctypes.c_int
     lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
@@ -154,6 +156,33 @@ def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custo
         _ptr(kv_cache), kv_cache.stride(0),
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         batch, num_draft, H, float(sm_scale), nsplit, dt,
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream), algo, min_chunk)
+    _check(st)
+
+
+def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                  qo_indptr, sm_scale: float, nsplit: int, out, lse, workspace, max_draft: int,
+                  algo: int = ALGO_AUTO, min_chunk: int = 0, stream=None) -> None:
+    """Enqueue tvmla_verify_ragged: request b has qo_indptr[b+1] - qo_indptr[b]
+    draft tokens (at most max_draft); q/out/lse hold qo_indptr[batch] token rows."""
+    ntok, H, dl = q_nope.shape
+    if dl != D_LATENT or tuple(q_rope.shape) != (ntok, H, D_ROPE):
+        raise TvmlaError(2, "q_nope must be [tok, H, 512] and q_rope [tok, H, 64]")
+    if q_nope.stride(2) != 1 or q_rope.stride(2) != 1 or kv_cache.stride(1) != 1:
+        raise TvmlaError(5, "last dimensions must be contiguous")
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise TvmlaError(5, "out and lse must be contiguous")
+    dt = _dtype_code(q_nope)
+    if q_rope.dtype != q_nope.dtype or kv_cache.dtype != q_nope.dtype or out.dtype != q_nope.dtype:
+        raise TvmlaError(3, "q_nope, q_rope, kv_cache and out must share one dtype")
+    batch = kv_indptr.numel() - 1
+    st = load().tvmla_verify_ragged(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0),
+        _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
+        _ptr(qo_indptr), batch, max_draft, H, float(sm_scale), nsplit, dt,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_ptr(stream), algo, min_chunk)
     _check(st)

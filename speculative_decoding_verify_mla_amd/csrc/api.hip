@@ -109,6 +109,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   char* ws = static_cast<char*>(workspace);
   p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
   p.lse_part = reinterpret_cast<float*>(ws + wl.lse_off);
+  p.qo_indptr = nullptr;
   return TVMLA_OK;
 }
 
@@ -118,20 +119,22 @@ static hipError_t launch_split(const SplitParams& p, int32_t algo, int32_t dtype
   return launch_split_scalar_fp32(p, s);
 }
 
-tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
-                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
-                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
-                             const int32_t* kv_indices, const int32_t* out_cache_loc,
-                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
-                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
-                             int32_t dtype, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+// Split + combine; qo_indptr null = num_draft tokens per request.
+static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
+                                int32_t batch, int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                                int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream, int32_t algo, int32_t min_chunk) {
   SplitParams p;
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
                             q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
                             custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse,
                             true, workspace, workspace_bytes, algo, min_chunk, p);
   if (st != TVMLA_OK) return st;
+  p.qo_indptr = qo_indptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_split(p, algo, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
 
@@ -144,10 +147,40 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
   c.num_heads = num_heads;
   c.nsplit = nsplit;
   c.min_chunk = min_chunk;
+  c.qo_indptr = qo_indptr;
   c.out = out;
   c.lse = lse;
   if (launch_combine(c, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
   return TVMLA_OK;
+}
+
+tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                             const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                             const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* out_cache_loc,
+                             const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                             int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                             int32_t dtype, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+  return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
+                     kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                     nullptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
+                     workspace_bytes, stream, algo, min_chunk);
+}
+
+tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                 const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                 const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                 const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
+                                 int32_t batch, int32_t max_draft, int32_t num_heads, float sm_scale,
+                                 int32_t nsplit, int32_t dtype, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+  if (!qo_indptr) return TVMLA_E_NULLPTR;
+  return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
+                     kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                     qo_indptr, batch, max_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
+                     workspace_bytes, stream, algo, min_chunk);
 }
 
 tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
@@ -204,6 +237,7 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
   c.num_heads = num_heads;
   c.nsplit = nsplit;
   c.min_chunk = min_chunk;
+  c.qo_indptr = nullptr;
   c.out = out;
   c.lse = lse;
   if (launch_combine(c, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;

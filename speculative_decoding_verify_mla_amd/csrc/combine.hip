@@ -51,10 +51,15 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
   if (row >= (int64_t)c.batch * R) return;  // only with W = 1; no barrier follows then
   const int b = (int)(row / R);
   const int r = (int)(row - (int64_t)b * R);
+  int Tb;
+  int64_t tb;  // draft tokens of request b, and the first one
+  request_tokens(c.qo_indptr, c.num_draft, b, Tb, tb);
+  if (r >= Tb * c.num_heads) return;  // one row per workgroup when W > 1: no barrier is left behind
+  const int64_t orow = tb * c.num_heads + r;  // output row
 
   int ns = c.nsplit;
   if (c.kv_indptr != nullptr) {
-    const int n = c.kv_indptr[b + 1] - c.kv_indptr[b] + c.num_draft;
+    const int n = c.kv_indptr[b + 1] - c.kv_indptr[b] + Tb;
     ns = active_splits(n, c.nsplit, c.min_chunk);
   }
   const size_t base = (size_t)b * c.nsplit * R + r;  // partial row of split 0
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
   }
 
   if (kBf16) {
-    uint16_t* dst = static_cast<uint16_t*>(c.out) + row * kDLatent + 8 * lane;
+    uint16_t* dst = static_cast<uint16_t*>(c.out) + orow * kDLatent + 8 * lane;
     uint4 u;
     u.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
     u.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
@@ -130,11 +135,11 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
     u.w = (uint32_t)f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
     *reinterpret_cast<uint4*>(dst) = u;
   } else {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(c.out) + row * kDLatent + 8 * lane);
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(c.out) + orow * kDLatent + 8 * lane);
     dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
-  if (lane == 0) c.lse[row] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
+  if (lane == 0) c.lse[orow] = mx != -INFINITY ? mx + logf(wsum) : -INFINITY;
 }
 
 template <int W>

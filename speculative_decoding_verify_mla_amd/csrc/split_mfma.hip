@@ -225,10 +225,15 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   const int b = pair / p.nsplit;
   const int s = pair - b * p.nsplit;
 
-  const int R = p.num_draft * p.num_heads;
+  const int Rw = p.num_draft * p.num_heads;  // partial-row stride of the workspace
+  int Tb;
+  int64_t tb;  // draft tokens of request b, and the first one
+  request_tokens(p.qo_indptr, p.num_draft, b, Tb, tb);
+  const int R = Tb * p.num_heads;
+  if (g * kRowsWG >= R) return;  // a shorter tree leaves this row group empty
   const int ip0 = p.kv_indptr[b];
   const int P = p.kv_indptr[b + 1] - ip0;
-  const int N = P + p.num_draft;
+  const int N = P + Tb;
   int start, end;
   split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
   if (start >= end) return;
@@ -239,7 +244,6 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   const int col = lane & 31;  // MFMA column = query row within the row block
   const int rb = wave & 1;    // row block whose scores this wavefront computes
   const int kh = wave >> 1;   // key half of each tile it scores
-  const int64_t tb = (int64_t)b * p.num_draft;  // first draft token of request b
 
   // This lane's scoring row. A row past the end computes on row R-1's data
   // (each MFMA column is independent) and is never written.
@@ -580,7 +584,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   auto write_block = [&](const f32x16_t (&ox)[4], float mref, float lrow, int x) {
     const int row = g * kRowsWG + 32 * x + col;
     if (row >= R) return;
-    const size_t prow = ((size_t)b * p.nsplit + s) * R + row;
+    const size_t prow = ((size_t)b * p.nsplit + s) * Rw + row;
     float* dst = p.o_part + prow * kDLatent + 128 * wave + 4 * hf;
     const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
 #pragma unroll

@@ -65,22 +65,25 @@ template <typename T>
 __global__ __launch_bounds__(256) void split_scalar_kernel(SplitParams p) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int R = p.num_draft * p.num_heads;
+  const int Rw = p.num_draft * p.num_heads;  // partial-row stride of the workspace
   const int r = blockIdx.x * 4 + wave;
   const int s = blockIdx.y;
   const int b = blockIdx.z;
-  if (r >= R) return;
+  int Tb;
+  int64_t tb;  // draft tokens of request b, and the first one
+  request_tokens(p.qo_indptr, p.num_draft, b, Tb, tb);
+  if (r >= Tb * p.num_heads) return;
 
   const int ip0 = p.kv_indptr[b];
   const int P = p.kv_indptr[b + 1] - ip0;
-  const int N = P + p.num_draft;
+  const int N = P + Tb;
   int start, end;
   split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
   if (start >= end) return;  // empty split: nothing to write, the combine skips it
 
   const int i = r / p.num_heads;
   const int h = r - i * p.num_heads;
-  const int64_t t = (int64_t)b * p.num_draft + i;
+  const int64_t t = tb + i;
 
   const T* qn = static_cast<const T*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head;
   const T* qr = static_cast<const T*>(p.q_rope) + t * p.qr_stride_tok + h * p.qr_stride_head;
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(SplitParams p) {
     m = mn;
   }
 
-  const size_t prow = ((size_t)b * p.nsplit + s) * R + r;
+  const size_t prow = ((size_t)b * p.nsplit + s) * Rw + r;
   float* dst = p.o_part + prow * kDLatent + 8 * lane;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   float4 a, c;

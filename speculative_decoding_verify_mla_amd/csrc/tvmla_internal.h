@@ -28,8 +28,9 @@ struct SplitParams {
   const int32_t* mask_indptr;
   int32_t batch, num_draft, num_heads, nsplit, min_chunk;
   float sm_scale;
-  float* o_part;    // [batch][nsplit][R][512]
-  float* lse_part;  // [batch][nsplit][R]
+  float* o_part;    // [batch][nsplit][num_draft * num_heads][512]
+  float* lse_part;  // [batch][nsplit][num_draft * num_heads]
+  const int64_t* qo_indptr;  // null: num_draft tokens per request; else per-request token ranges
 };
 
 struct CombineParams {
@@ -37,6 +38,7 @@ struct CombineParams {
   const float* lse_part;
   const int32_t* kv_indptr;  // may be null: read every split
   int32_t batch, num_draft, num_heads, nsplit, min_chunk;
+  const int64_t* qo_indptr;  // null: num_draft tokens per request; else per-request token ranges
   void* out;
   float* lse;
 };
@@ -94,6 +96,20 @@ __host__ __device__ inline int active_splits(int n, int nsplit, int min_chunk) {
   if (chunk < min_chunk) chunk = min_chunk;
   const int a = (n + chunk - 1) / chunk;
   return a < nsplit ? a : nsplit;
+}
+
+// Draft tokens of request b and the index of its first one: num_draft and
+// b * num_draft, or with qo_indptr its range qo_indptr[b] .. qo_indptr[b+1]
+// (the count clamped to [0, num_draft]).
+__device__ inline void request_tokens(const int64_t* qo_indptr, int num_draft, int b, int& Tb, int64_t& t0) {
+  if (qo_indptr == nullptr) {
+    Tb = num_draft;
+    t0 = (int64_t)b * num_draft;
+    return;
+  }
+  t0 = qo_indptr[b];
+  const int64_t n = qo_indptr[b + 1] - t0;
+  Tb = n < 0 ? 0 : (n > num_draft ? num_draft : (int)n);
 }
 
 // Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).

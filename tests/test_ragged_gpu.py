@@ -1,0 +1,71 @@
+"""GPU parity of tvmla_verify_ragged (draft trees of different sizes per
+request) against the fp64 oracle, and bit-identity with tvmla_verify when
+every request keeps its whole tree."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import Device, compare, log
+from oracle import verify_fp64 as vo
+from speculative_decoding_verify_mla_amd import binding
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, r, algo=binding.ALGO_AUTO, nsplit=None):
+    dev = "cuda"
+    ns = nsplit or w.spec.nsplit
+    pool = w.device_pool(dev, fill=float("nan"))
+    ntok, H = r.q_nope.shape[0], w.num_heads
+    out = torch.full((max(ntok, 1), H, 512), float("nan"), dtype=w.torch_dtype, device=dev)
+    lse = torch.full((max(ntok, 1), H), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.full((binding.workspace_bytes(w.batch, w.num_draft, H, ns) // 4,), float("nan"),
+                    dtype=torch.float32, device=dev)
+    kv_indices = w.kv_indices.to(dev) if w.kv_indices.numel() else torch.zeros(1, dtype=torch.int32, device=dev)
+    ocl = r.out_cache_loc.to(dev) if r.out_cache_loc.numel() else torch.zeros(1, dtype=torch.int32, device=dev)
+    mask = r.custom_mask.to(dev) if r.custom_mask.numel() else torch.zeros(1, dtype=torch.uint8, device=dev)
+    qn = r.q_nope.to(dev) if ntok else torch.zeros((1, H, 512), dtype=w.torch_dtype, device=dev)
+    qr = r.q_rope.to(dev) if ntok else torch.zeros((1, H, 64), dtype=w.torch_dtype, device=dev)
+    binding.verify_ragged(qn, qr, pool, w.kv_indptr.to(dev), kv_indices, ocl, mask, r.mask_indptr.to(dev),
+                          r.qo_indptr.to(dev), w.sm_scale, ns, out, lse, ws, w.num_draft, algo=algo)
+    torch.cuda.synchronize()
+    return out[:ntok].float().cpu().numpy().astype(np.float64), lse[:ntok].cpu().numpy().astype(np.float64)
+
+
+CASES = {
+    "rag_bf16": (dict(batch=5, prefix=(0, 3000), num_draft=9, num_heads=16, dtype="bf16", tree="random",
+                      pool_slots=1 << 16, layout="scattered", nsplit=16, seed=41), [9, 0, 1, 5, 8]),
+    "rag_bf16_h64": (dict(batch=3, prefix=(100, 5000), num_draft=16, num_heads=64, dtype="bf16", tree="random",
+                          pool_slots=1 << 16, layout="scattered", nsplit=64, seed=42), [3, 16, 11]),
+    "rag_fp32": (dict(batch=4, prefix=(0, 700), num_draft=7, num_heads=4, dtype="fp32", tree="chain",
+                      pool_slots=1 << 14, layout="scattered", nsplit=8, seed=43), [7, 2, 0, 6]),
+    "rag_all_empty": (dict(batch=2, prefix=(10, 20), num_draft=4, num_heads=8, dtype="bf16", tree="random",
+                           pool_slots=1 << 10, layout="scattered", nsplit=4, seed=44), [0, 0]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("algo", [binding.ALGO_AUTO, binding.ALGO_SCALAR])
+def test_ragged_matches_oracle(name, algo):
+    kw, tokens = CASES[name]
+    w = gen.build(gen.small(name, **kw))
+    r = gen.ragged_trees(w, tokens)
+    log(f"ragged case {name} algo {algo}: tokens {tokens}")
+    out, lse = _run(w, r, algo=algo)
+    if sum(tokens) == 0:
+        return
+    ref_o, ref_l = vo.verify_ragged(r.q_nope, r.q_rope, w.host_pool(fill=0.0), w.kv_indptr, w.kv_indices,
+                                    r.out_cache_loc, r.custom_mask, r.mask_indptr, r.qo_indptr, w.sm_scale)
+    compare(w, out, lse, ref_o, ref_l, f"{name}/algo{algo}")
+
+
+def test_whole_trees_equal_fixed_verify():
+    kw, _ = CASES["rag_bf16_h64"]
+    w = gen.build(gen.small("rag_whole", **kw))
+    r = gen.ragged_trees(w, [w.num_draft] * w.batch)
+    log("ragged case: whole trees vs tvmla_verify")
+    out, lse = _run(w, r)
+    d = Device(w)
+    out0, lse0 = d.result()
+    assert np.array_equal(out, out0) and np.array_equal(lse, lse0)

@@ -263,3 +263,47 @@ def small(name: str, batch: int, prefix, num_draft: int, num_heads: int, dtype: 
           nsplit: int = 64, seed: int = 7) -> Spec:
     """A custom spec for tests (ragged tails, tiny heads, empty prefixes, ...)."""
     return Spec(name, batch, prefix, num_draft, tree, num_heads, dtype, pool_slots, layout, nsplit, seed)
+
+
+@dataclass
+class RaggedTrees:
+    """A workload whose request b keeps only the first T_b of its draft nodes
+    (a valid subtree: parents precede children). Arrays in the layout of the
+    ragged verify call: token offsets qo_indptr, draft slots, mask blocks
+    [T_b][P_b + T_b] and queries for the kept tokens only."""
+    base: Workload
+    tokens: np.ndarray  # int64 [batch]: T_b
+    qo_indptr: torch.Tensor  # int64 [batch+1]
+    q_nope: torch.Tensor  # [sum T_b, H, 512]
+    q_rope: torch.Tensor  # [sum T_b, H, 64]
+    out_cache_loc: torch.Tensor  # int32 [sum T_b]
+    custom_mask: torch.Tensor  # uint8 [sum T_b * (P_b + T_b)]
+    mask_indptr: torch.Tensor  # int32 [batch+1]
+
+
+def ragged_trees(w: Workload, tokens) -> RaggedTrees:
+    """Cut request b's tree of w to its first tokens[b] nodes (0 <= T_b <= T)."""
+    T = w.num_draft
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if tokens.shape != (w.batch,) or (tokens < 0).any() or (tokens > T).any():
+        raise ValueError("need one token count in [0, num_draft] per request")
+    qo = np.zeros(w.batch + 1, dtype=np.int64)
+    qo[1:] = np.cumsum(tokens)
+    keep = np.concatenate([np.arange(b * T, b * T + tokens[b]) for b in range(w.batch)]).astype(np.int64)
+    ocl = w.out_cache_loc.numpy()[keep]
+    masks, mind = [], np.zeros(w.batch + 1, dtype=np.int64)
+    full = w.custom_mask.numpy()
+    for b in range(w.batch):
+        P, Tb = int(w.prefix_lens[b]), int(tokens[b])
+        blk = full[int(w.mask_indptr[b]):int(w.mask_indptr[b + 1])].reshape(T, P + T)
+        m = np.ascontiguousarray(blk[:Tb, :P + Tb])
+        masks.append(m.reshape(-1))
+        mind[b + 1] = mind[b] + m.size
+    idx = torch.from_numpy(keep)
+    return RaggedTrees(
+        base=w, tokens=tokens, qo_indptr=torch.from_numpy(qo),
+        q_nope=w.q_nope[idx].contiguous(), q_rope=w.q_rope[idx].contiguous(),
+        out_cache_loc=torch.from_numpy(ocl.astype(np.int32)),
+        custom_mask=torch.from_numpy(np.concatenate(masks) if masks else np.zeros(0, np.uint8)),
+        mask_indptr=torch.from_numpy(mind.astype(np.int32)),
+    )
