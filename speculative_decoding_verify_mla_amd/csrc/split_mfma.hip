@@ -177,25 +177,22 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 // time over the previous tile's compute (a burst of loads would stall the
 // issuing wavefront until the texture path drains it). slot_reg holds, in
 // lane k, the cache slot of the tile's key k.
-//   latent: key k = 16 wave + u (u = 0..15); a buffer resource over the key's
-//           cache row, whose address lane k holds in (ra_hi, ra_lo) (its
-//           1152-byte size also bounds the read), and lane l loads piece
-//           l ^ swz(k) into LDS piece l of the key's 1024-byte latent row;
+//   latent: key k = 16 wave + u (u = 0..15); the key's cache-row address,
+//           which lane k holds in (ra_hi, ra_lo), goes to scalar registers
+//           as the load's base and lane l loads piece l ^ swz(k) (a 32-bit
+//           lane offset) into LDS piece l of the key's 1024-byte latent row;
 //   rope:   keys 8v..8v+7 (v = 2 wave + u, u = 0..1), 128 contiguous bytes
 //           each: lane l serves key k = 8v + l/8 and stores its 16-byte
 //           piece (l%8) ^ (k%8) at position l%8 of the key's 128-byte rope
 //           row, so a score read of one piece over 8 consecutive keys hits
 //           8 different bank groups. `row` is lane l's source row, the
 //           cache row of key k (fetched from lane k with a lane shuffle).
-constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data format
-
 __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
   const int k = 16 * wave + u;  // swz(k) depends on u only
   const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
-  const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)row_addr, 0, kDKey * 2, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(row, TVMLA_LDS(void, dst + k * kLatRow), 16, (lane ^ piece_swz(k)) << 4,
-                                           0, 0, 0);
+  const char* src = reinterpret_cast<const char*>(row_addr) + ((lane ^ piece_swz(k)) << 4);
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 0);
 }
 
 __device__ __forceinline__ void stage_rope(char* dst, const char* row, int wave, int lane, int u) {
