@@ -49,6 +49,8 @@ SMALL = {
     "chain_h16": gen.small("chain_h16", 2, [700, 65], 8, 16, tree="chain", seed=16),
     # fp32 through the scalar kernel, ragged
     "fp32_ragged": gen.small("fp32_ragged", 3, [0, 9, 130], 4, 8, dtype="fp32", seed=17),
+    # many short requests: 19,200 (request, split) pairs, 7,200 output rows (one combine wavefront each)
+    "many_requests": gen.small("many_requests", 300, (0, 64), 3, 8, pool_slots=1 << 15, seed=18),
 }
 
 
@@ -74,7 +76,7 @@ def test_small_cases_full(name):
         compare(w, out, lse, ref_out, ref_lse, f"{name}/algo{algo}")
 
 
-@pytest.mark.parametrize("nsplit", [1, 3, 64, 200])
+@pytest.mark.parametrize("nsplit", [1, 3, 64, 200, 256])
 def test_nsplit_invariance(nsplit):
     w = gen.build("p4096")
     ref_out, ref_lse = _oracle(w)
