@@ -208,7 +208,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="long185k")
-    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma")
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 scalar, 2 mfma (64 rows), 3 mfma (128 rows)")
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--nsplit", type=int, default=0, help="override the workload's split count (diagnostics)")
     ap.add_argument("--op", default="verify", choices=["verify", "defrag", "tree_mask"],

@@ -69,7 +69,9 @@ typedef enum {
 typedef enum {
   TVMLA_ALGO_AUTO = 0,   /* bf16 -> MFMA kernel, fp32 -> scalar kernel          */
   TVMLA_ALGO_SCALAR = 1, /* one wavefront per (row, split); fp32 FMA; any dtype */
-  TVMLA_ALGO_MFMA = 2    /* bf16 MFMA kernel; bf16 only                         */
+  TVMLA_ALGO_MFMA = 2,   /* bf16 MFMA kernel, 64 query rows per workgroup       */
+  TVMLA_ALGO_ROWS = 3    /* bf16 MFMA kernel, 128 query rows per workgroup, each
+                            wavefront owning 32 rows outright; bf16 only       */
 } tvmla_algo;
 
 /*

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtvmla.so")
 
 BF16, FP32 = 0, 1
-ALGO_AUTO, ALGO_SCALAR, ALGO_MFMA = 0, 1, 2
+ALGO_AUTO, ALGO_SCALAR, ALGO_MFMA, ALGO_ROWS = 0, 1, 2, 3
 D_LATENT, D_ROPE, D_KEY = 512, 64, 576
 
 STATUS = {

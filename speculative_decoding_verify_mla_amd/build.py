@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libtvmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "split_scalar.hip", "split_mfma.hip", "combine.hip", "defrag.hip", "tree_mask.hip"]
+SOURCES = ["api.hip", "split_scalar.hip", "split_mfma.hip", "split_rows.hip", "combine.hip", "defrag.hip", "tree_mask.hip"]
 
 # Per-file flags. The MFMA split kernel keeps its accumulators in VGPRs
 # (MFMA destination/accumulator in the VGPR file) so the online-softmax
@@ -68,7 +68,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         out = _run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj, out
 
-    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         results = list(ex.map(one, SOURCES))
     if resource_usage:
         for _, out in results:

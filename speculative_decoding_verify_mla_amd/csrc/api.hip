@@ -11,6 +11,8 @@
 #include "../../include/tvmla.h"
 #include "tvmla_internal.h"
 
+#include <stdlib.h>
+
 using namespace tvmla;
 
 namespace {
@@ -23,6 +25,21 @@ tvmla_status check_shape(int32_t batch, int32_t num_draft, int32_t num_heads, in
   if (num_heads < 1 || num_heads > TVMLA_MAX_HEADS) return TVMLA_E_SHAPE;
   if (nsplit < 1 || nsplit > TVMLA_MAX_NSPLIT) return TVMLA_E_SHAPE;
   return TVMLA_OK;
+}
+
+// Growth of a row's running max (log2 units) past which the row-owner
+// kernel folds its accumulator into the workspace (16: probabilities stay
+// below 2^16). TVMLA_FOLD_LOG2 overrides it, read at every call; results are
+// the same for any value >= 0, only the number of folds changes, which lets
+// tests drive the fold path on ordinary data.
+float fold_log2() {
+  const char* env = getenv("TVMLA_FOLD_LOG2");
+  if (env && *env) {
+    char* endp = nullptr;
+    const float v = strtof(env, &endp);
+    if (endp != env && v >= 0.f && v < INFINITY) return v;
+  }
+  return 16.f;
 }
 
 }  // namespace
@@ -62,9 +79,10 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
                             bool need_out, void* workspace, size_t workspace_bytes, int32_t& algo,
                             int32_t min_chunk, SplitParams& p) {
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
-  if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA) return TVMLA_E_ALGO;
+  if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA && algo != TVMLA_ALGO_ROWS)
+    return TVMLA_E_ALGO;
   if (algo == TVMLA_ALGO_AUTO) algo = dtype == TVMLA_BF16 ? TVMLA_ALGO_MFMA : TVMLA_ALGO_SCALAR;
-  if (algo == TVMLA_ALGO_MFMA && dtype != TVMLA_BF16) return TVMLA_E_DTYPE;
+  if ((algo == TVMLA_ALGO_MFMA || algo == TVMLA_ALGO_ROWS) && dtype != TVMLA_BF16) return TVMLA_E_DTYPE;
   if (!q_nope || !q_rope || !kv_cache || !kv_indptr || !kv_indices || !out_cache_loc || !custom_mask ||
       !mask_indptr)
     return TVMLA_E_NULLPTR;
@@ -110,11 +128,13 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
   p.lse_part = reinterpret_cast<float*>(ws + wl.lse_off);
   p.qo_indptr = nullptr;
+  p.fold_log2 = fold_log2();
   return TVMLA_OK;
 }
 
 static hipError_t launch_split(const SplitParams& p, int32_t algo, int32_t dtype, hipStream_t s) {
   if (algo == TVMLA_ALGO_MFMA) return launch_split_mfma_bf16(p, s);
+  if (algo == TVMLA_ALGO_ROWS) return launch_split_rows_bf16(p, s);
   if (dtype == TVMLA_BF16) return launch_split_scalar_bf16(p, s);
   return launch_split_scalar_fp32(p, s);
 }

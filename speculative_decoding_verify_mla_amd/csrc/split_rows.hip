@@ -1,0 +1,585 @@
+// bf16 MFMA split kernel for gfx950, row-owner form.
+//
+// Work unit: one workgroup = (request b, split s, group of 128 query rows).
+// Wavefront w owns rows 32w .. 32w+31 of the group outright: it scores them
+// against all 64 keys of every tile, keeps their softmax state, and
+// accumulates their whole 512-entry output. Rows are r = i*H + h (draft token
+// i, head h); every row of a request attends to the same keys, so one key
+// tile staged in LDS feeds all 128 rows of the group ("The Plan Document",
+// section "The Design Reasoning", variants 2 and 3: read the shared latent
+// once, use it for many heads).
+//
+// LDS tile format, staging and value reads are those of the 64-row kernel:
+// a 64-key tile is a latent region (64 keys x 1024 bytes, the 16-byte pieces
+// of a key XOR-swizzled by a function of the key) and a rope region (64 keys
+// x 128 bytes), filled by direct global->LDS loads one tile ahead into a
+// second buffer.
+//
+// Per tile, wavefront w:
+//   scores   S^T = K Q^T for keys 0..31 and 32..63 of the tile (two 32x32
+//            blocks, 36 k-steps each, v_mfma_f32_32x32x16_bf16; A = key rows
+//            read from LDS, B = the wavefront's 32 queries, held in VGPRs for
+//            the whole split);
+//   softmax  each lane holds 32 of its row's 64 scores, so the row maximum is
+//            a register maximum and one swap of lane halves -- no LDS
+//            exchange and no barrier. The probabilities, rounded to bf16,
+//            already sit in the lanes and order the value product takes as
+//            its B operand;
+//   values   O^T += V^T P^T over all 512 latent entries (16 entry blocks x 4
+//            key steps of 16), V^T read with the transposed LDS read
+//            (ds_read_b64_tr_b16). O^T (512 x 32 fp32) lives in the 256
+//            AGPRs for the whole split.
+// Against the 64-row kernel this halves the staging loads and tile barriers
+// per row and drops the probability exchange; in exchange every wavefront
+// reads the whole tile from LDS (about 136 KB per wavefront per tile).
+//
+// Split bounds, key slots, mask bytes and P_b follow page 1, "The Design
+// Emerges" (chunk = ceil(N / nsplit), empty split returns at once; slot from
+// kv_indices for the prefix and out_cache_loc for draft keys; mask byte
+// custom_mask[mask_indptr[b] + i*N + p]; P_b from kv_indptr). The online
+// softmax (page 1, "Input Knowledge Required": running max, running sum,
+// rescaled accumulator) keeps a per-row reference max and leaves the
+// accumulator alone while the row's max stays within 2^fold_log2 of it
+// (fold_log2 = 16: every probability stays below 65,536). When a row
+// outgrows that, the wavefront folds: the accumulator goes to the rows'
+// partial-result slots in the workspace (adding in what earlier folds left
+// there, brought to the current reference), restarts from zero, and the
+// reference moves up. The accumulator is never touched by vector
+// instructions inside the tile loop -- only by MFMAs and by stores that read
+// it straight from the AGPRs -- which is what keeps the compiler from moving
+// it to VGPRs. The normalised result is the same for any threshold.
+
+#include "tvmla_internal.h"
+
+namespace tvmla {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+#define TVMLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+constexpr int kRowsWG = 128;  // query rows per workgroup (4 wavefronts x 32)
+constexpr int kKT = 64;       // keys per tile
+constexpr int kLatRow = 1024; // bytes of one key's latent part in LDS (64 pieces of 16 B)
+constexpr int kRopeRow = 128; // bytes of one key's rope part in LDS (8 pieces of 16 B)
+constexpr int kTileLat = kKT * kLatRow;
+constexpr int kTileBytes = kTileLat + kKT * kRopeRow;  // 73,728 bytes per tile buffer
+constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
+constexpr int kSSteps = 2 * kQSteps;                   // score MFMAs per tile (two key blocks)
+constexpr int kVSteps = 64;                            // value MFMAs per tile (16 entry blocks x 4 key steps)
+constexpr int kSRing = 4;                              // score operand reads in flight
+constexpr int kVRing = 4;                              // value steps in flight (two reads each)
+
+// Piece swizzle of key k: key bits 0..1 to piece bits 2..3, key bits 2..3
+// to piece bits 0..1 (see the 64-row kernel: a permutation over any 16
+// consecutive keys, and 16 distinct slots for each transposed read cycle).
+__host__ __device__ constexpr int piece_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+constexpr int kSwzHi = piece_swz(8) ^ piece_swz(0);  // swz(k + 8) ^ swz(k) for k % 16 < 8
+
+template <int I>
+struct Int {
+  static constexpr int value = I;
+};
+// Compile-time loop: f(Int<i>) for i in [B, E); the index is a constant
+// expression inside f, as the immediate operands of the inline asm need.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Barrier at the top of a tile: this wavefront's loads into the tile have
+// landed (vmcnt(0) expcnt(7) lgkmcnt(0) in the gfx9 encoding, via the
+// builtin so the compiler knows every earlier load completed) and, after
+// the barrier, so have everyone else's.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Workgroup barrier after this wavefront's LDS operations (not its global
+// loads) have completed.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS operand reads through inline asm with an immediate offset. The
+// compiler would treat its own LDS loads as possibly aliasing the in-flight
+// direct-to-LDS loads and wait for all of them first; these reads are
+// waited for explicitly (lgkmcnt) by the caller before use. LDS operations
+// complete in order, so "at most n outstanding" after a read means the read
+// is done once n later ones were issued.
+template <int Off>
+__device__ __forceinline__ bf16x8_t read_b128(uint32_t addr) {
+  bf16x8_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(Off));
+  return r;
+}
+template <int Off>
+__device__ __forceinline__ i16x4_t read_tr(uint32_t addr) {
+  i16x4_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(Off));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm(bf16x8_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm2(i16x4_t& a, i16x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
+// Score MFMA (accumulator in VGPRs, read by the softmax) and value MFMA
+// (accumulator in AGPRs). Inline asm keeps the operands where they are; the
+// compiler cannot see the hazards through it, so they are spelled out:
+// TVMLA_S_DRAIN before vector code reads a score (24 wait states, twice
+// what 8 passes need), and "s_nop 1" (2 wait states) in front of an MFMA
+// whose operand may have just been written by a vector ALU instruction.
+#define TVMLA_MFMA_S_FIRST(acc, a, q) \
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(q))
+#define TVMLA_MFMA_S(acc, a, q) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q))
+#define TVMLA_MFMA_O(acc, a, p) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p))
+#define TVMLA_MFMA_O_NOP(acc, a, p) \
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p))
+#define TVMLA_MFMA_ZERO(acc, z) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z))
+#define TVMLA_S_DRAIN(s0, s1) asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s0), "+v"(s1))
+#define TVMLA_O_DRAIN(o)                                                                                          \
+  asm volatile("s_nop 15\n\ts_nop 7"                                                                            \
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), \
+                 "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),        \
+                 "+a"(o[15]))
+
+// Partial-result slot of a row: 512 fp32 latent entries. A lane's 16
+// accumulator values of entry block db sit in four runs of 4 floats at
+// stride 8 (entries 32db + 8jg + 4hf ..).
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+template <int J>
+__device__ __forceinline__ f32x4_t quad(const f32x16_t& o) {
+  return __builtin_shufflevector(o, o, 4 * J, 4 * J + 1, 4 * J + 2, 4 * J + 3);
+}
+// Plain stores of the accumulator quads: the compiler takes the data
+// straight from the AGPRs. (Reading the accumulator with vector
+// instructions inside the tile loop would make it keep the accumulator in
+// VGPRs instead.)
+__device__ __forceinline__ void store_block(float* slot, const f32x16_t& o) {
+  *reinterpret_cast<f32x4_t*>(slot) = quad<0>(o);
+  *reinterpret_cast<f32x4_t*>(slot + 8) = quad<1>(o);
+  *reinterpret_cast<f32x4_t*>(slot + 16) = quad<2>(o);
+  *reinterpret_cast<f32x4_t*>(slot + 24) = quad<3>(o);
+}
+
+#define TVMLA_MFMA_F32(acc, a, b) \
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x2_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b))
+
+// o^T += slot^T * diag(beta) for the wavefront's 32 rows, with fp32 MFMAs
+// (32x32x2): A = two rows' slot entries per step (lane (k, i) holds entry
+// 32db + i of row 2s + k), B = the matching two columns of diag(beta) (lane
+// (k, j) holds beta_j when j = 2s + k). Each product adds one slot value
+// times one beta, exactly as fp32 arithmetic does. `slot0` is the slot of
+// the wavefront's row 0; rows at or past `rows` have no slot and add zero.
+__device__ __forceinline__ void add_slots(f32x16_t (&o)[16], const float* slot0, int rows, float beta, int lane) {
+  const int i = lane & 31, k = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const int q = 2 * s2 + k;
+      const float a = q < rows ? __hip_atomic_load(slot0 + (size_t)q * kDLatent + 32 * db + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+      const float bb = i == q ? beta : 0.f;
+      TVMLA_MFMA_F32(o[db], a, bb);
+    }
+    asm volatile("" ::: "memory");  // one block's loads at a time
+  }
+}
+
+// An opaque copy of a value: addresses derived from it are computed where
+// they are used instead of being hoisted out of the tile loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
+  typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Direct-to-LDS staging of one 64-key tile, one load at a time over the
+// previous tile's score MFMAs. ra_lo/ra_hi hold, in lane k, the cache-row
+// address of the tile's key k.
+//   latent: key k = 16 wave + u; the row address goes to scalar registers as
+//           the load's base and lane l loads piece l ^ swz(k) into LDS piece
+//           l of the key's 1024-byte latent row;
+//   rope:   keys 8v..8v+7 (v = 2 wave + u): lane l serves key 8v + l/8 and
+//           stores its piece (l%8) ^ (k%8) at position l%8 of the key's
+//           128-byte rope row; `row` is that key's cache row.
+__device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
+  const int k = 16 * wave + u;
+  const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
+  const char* src = reinterpret_cast<const char*>(row_addr) + ((lane ^ piece_swz(k)) << 4);
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 0);
+}
+
+__device__ __forceinline__ void stage_rope(char* dst, const char* row, int wave, int lane, int u) {
+  const int v = 2 * wave + u;
+  const char* src = row + kDLatent * 2 + 16 * ((lane & 7) ^ (lane >> 3));
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void split_rows_kernel(SplitParams p, int groups, int pairs) {
+  __shared__ __attribute__((aligned(16))) char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char kb1[kTileBytes];
+
+  // Workgroup ids reach the 8 XCDs round-robin (id % 8); every row group of
+  // one (request, split) pair gets the same id % 8, so the pair's key rows
+  // come from HBM once and are re-read from that XCD's L2.
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int kq = id >> 3;
+  const int jq = kq / groups;
+  const int g = kq - jq * groups;
+  const int pair = xcd + 8 * jq;
+  if (pair >= pairs) return;
+  const int b = pair / p.nsplit;
+  const int s = pair - b * p.nsplit;
+
+  const int Rw = p.num_draft * p.num_heads;  // partial-row stride of the workspace
+  int Tb;
+  int64_t tb;
+  request_tokens(p.qo_indptr, p.num_draft, b, Tb, tb);
+  const int R = Tb * p.num_heads;
+  if (g * kRowsWG >= R) return;
+  const int ip0 = p.kv_indptr[b];
+  const int P = p.kv_indptr[b + 1] - ip0;
+  const int N = P + Tb;
+  int start, end;
+  split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
+  if (start >= end) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hf = lane >> 5;   // which 8-wide half of each 16-wide k-step this lane feeds
+  const int col = lane & 31;  // MFMA column = query row within the wavefront
+
+  // This lane's row. Rows past the end compute on row R-1's data (MFMA
+  // columns are independent) and are never written.
+  const int r = g * kRowsWG + 32 * wave + col;
+  const int rr = r < R ? r : R - 1;
+  const int i = rr / p.num_heads;
+  const int h = rr - i * p.num_heads;
+  const int64_t t = tb + i;
+
+  // Q^T operands: the lane's row, key entries [16ks + 8hf, +8).
+  bf16x8_t qf[kQSteps];
+  {
+    const uint16_t* qn = static_cast<const uint16_t*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head + 8 * hf;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + t * p.qr_stride_tok + h * p.qr_stride_head + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < kDLatent / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qn + 16 * ks));
+#pragma unroll
+    for (int ks = 0; ks < kDRope / 16; ++ks)
+      qf[kDLatent / 16 + ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * ks));
+  }
+
+  f32x16_t o[16];  // O^T blocks: latent entries [32db, 32db + 32) x the 32 rows
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+  float m_ref = -INFINITY;  // the row's reference max (log2 units); both lane halves agree
+  float l_part = 0.f;       // this lane's share of its row's softmax sum (since the last fold)
+  float l_fold = 0.f;       // this lane's share of the folded sum (against m_slot)
+  float m_slot = 0.f;       // the reference of the slot's folded sum
+  bool folded = false;      // the partial-result slot holds a folded accumulator (wavefront-uniform)
+  const bf16x8_t zero8 = {};
+  const size_t prow = ((size_t)b * p.nsplit + s) * Rw + r;  // partial-result row (valid when r < R)
+  float* fold_dst = p.o_part + prow * kDLatent + 4 * hf;
+  const float* slot0 = p.o_part + (prow - col) * kDLatent;  // slot of the wavefront's row 0
+  const int rows_valid = min(32, R - (g * kRowsWG + 32 * wave));
+
+  const float scale2 = p.sm_scale * kLog2e;
+  const char* kvb = static_cast<const char*>(p.kv);
+  const int64_t row_bytes = p.kv_stride * 2;
+
+  // Slot of key `key`; keys past the split's end re-read the last key
+  // (finite data whose probability is forced to zero).
+  auto slot_of = [&](int key) -> int {
+    key = key < end ? key : end - 1;
+    const int32_t* src = key < P ? p.kv_indices + ip0 + key : p.out_cache_loc + tb + (key - P);
+    return *src;
+  };
+  // Visibility. The wavefront's 32 rows belong to draft tokens tok0 ..
+  // tok0+ntok-1 (one token when H is a multiple of 32). Lane k reads the
+  // mask byte of tile key k for each such token and a ballot turns the 64
+  // bytes into a bit mask; each lane keeps its own token's. Bytes for four
+  // tokens are prefetched a tile ahead; more tokens (fewer than eight heads)
+  // are read when needed.
+  const int rfirst = min(g * kRowsWG + 32 * wave, R - 1);
+  const int rlast = min(g * kRowsWG + 32 * wave + 31, R - 1);
+  const int tok0 = rfirst / p.num_heads;
+  const int ntok = rlast / p.num_heads - tok0 + 1;
+  const int my_u = i - tok0;
+  const uint8_t* mbase = p.mask + p.mask_indptr[b] + (int64_t)tok0 * N;
+  uint8_t mnext[4];
+  auto load_mask = [&](int p0) {
+    int key = p0 + lane;
+    key = key < end ? key : end - 1;
+    mnext[0] = mbase[key];
+    if (ntok > 1) {
+#pragma unroll
+      for (int u = 1; u < 4; ++u) mnext[u] = mbase[(int64_t)min(u, ntok - 1) * N + key];
+    }
+  };
+  auto visible_bits = [&](int p0) -> uint64_t {  // bit k: tile key k visible to my row
+    const int key = p0 + lane;
+    const bool kok = key < end;
+    if (ntok == 1) return (uint64_t)__ballot(kok && mnext[0] != 0);
+    uint64_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t bal = (uint64_t)__ballot(kok && mnext[u] != 0);
+      mine = u == my_u ? bal : mine;
+    }
+    for (int u = 4; u < ntok; ++u) {
+      const uint64_t bal = (uint64_t)__ballot(kok && mbase[(int64_t)u * N + (kok ? key : end - 1)] != 0);
+      mine = u == my_u ? bal : mine;
+    }
+    return mine;
+  };
+
+  const int ntiles = (end - start + kKT - 1) / kKT;
+  int slot_reg = slot_of(start + lane);
+  auto row_address = [&](int slot, uint32_t& lo, uint32_t& hi) {
+    const uint64_t a = (uint64_t)(uintptr_t)(kvb + (int64_t)slot * row_bytes);
+    lo = (uint32_t)a;
+    hi = (uint32_t)(a >> 32);
+  };
+  {
+    uint32_t lo, hi;
+    row_address(slot_reg, lo, hi);
+#pragma unroll
+    for (int u = 0; u < kKT / 4; ++u) stage_key(kb0, lo, hi, wave, lane, u);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      stage_rope(kb0, kvb + (int64_t)__shfl(slot_reg, 8 * (2 * wave + u) + (lane >> 3), 64) * row_bytes, wave, lane,
+                 u);
+  }
+  load_mask(start);
+  slot_reg = slot_of(start + kKT + lane);
+
+  auto body = [&](int tile, const char* cur, char* nxt) {
+    const int p0 = start + tile * kKT;
+    const int ln = opaque(lane);
+    const uint64_t vis = visible_bits(p0);
+    load_mask(p0 + kKT);  // on the last tile these re-read clamped, valid bytes
+    const int slot_cur = slot_reg;
+    slot_reg = slot_of(p0 + 2 * kKT + lane);
+    uint32_t ra_lo, ra_hi;  // lane k: cache row address of the next tile's key k
+    row_address(slot_cur, ra_lo, ra_hi);
+    const int rslot0 = __shfl(slot_cur, 16 * wave + (ln >> 3), 64);
+    const int rslot1 = __shfl(slot_cur, 16 * wave + 8 + (ln >> 3), 64);
+
+    // ---- S^T = K Q^T, key block kb = n / 36, k-step ks = n % 36 (block 0's
+    // chain, then block 1's). Score operand of lane (hf, col): key 32kb +
+    // col, latent piece 2ks + hf stored at (2ks + hf) ^ swz(col) =
+    // 16(ks / 8) + ((2(ks % 8)) ^ sq), sq = swz(col) ^ hf; rope k-step
+    // 32 + c reads rope piece 2c + hf stored at (2c + hf) ^ (col % 8).
+    // The eight latent address patterns and two rope ones are registers;
+    // block, piece group and rope block are immediate offsets. The next
+    // tile's sixteen latent loads go one per four MFMAs.
+    const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
+    const int lcol = ln & 31, lhf = ln >> 5;
+    const int sq = piece_swz(lcol) ^ lhf;
+    const uint32_t kbase = cur_lds + lcol * kLatRow;
+    const uint32_t rbase = cur_lds + kTileLat + lcol * kRopeRow;
+    const int rsw = lhf ^ (lcol & 7);
+    auto saddr = [&](auto n_) -> uint32_t {
+      constexpr int n = decltype(n_)::value, ks = n % kQSteps;
+      if constexpr (ks < 32)
+        return kbase + (((2 * (ks % 8)) ^ sq) << 4);
+      else
+        return rbase + (((2 * (ks - 32)) ^ rsw) << 4);
+    };
+    auto sread = [&](auto n_) -> bf16x8_t {
+      constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
+      constexpr int off = ks < 32 ? kb * 32 * kLatRow + 256 * (ks / 8) : kb * 32 * kRopeRow;
+      return read_b128<off>(saddr(n_));
+    };
+    bf16x8_t ring[kSRing];
+    static_for<0, kSRing>([&](auto x_) { ring[decltype(x_)::value] = sread(x_); });
+    f32x16_t sacc[2];
+    static_for<0, kSSteps>([&](auto n_) {
+      constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
+      if constexpr (n % 4 == 1 && n / 4 < 16) stage_key(nxt, ra_lo, ra_hi, wave, ln, n / 4);
+      bf16x8_t& kf = ring[n % kSRing];
+      constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
+      wait_lgkm<ahead>(kf);
+      if constexpr (ks == 0)
+        TVMLA_MFMA_S_FIRST(sacc[kb], kf, qf[0]);
+      else
+        TVMLA_MFMA_S(sacc[kb], kf, qf[ks]);
+      if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
+    });
+    stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
+    stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
+
+    // ---- softmax over the tile. Masked scores become -inf (skipped when the
+    // whole wavefront sees every key). sm_scale > 0, so the maximum of the
+    // raw scores times scale2 is the maximum of the scaled scores exactly.
+    TVMLA_S_DRAIN(sacc[0], sacc[1]);
+    float sm[32];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      sm[j] = sacc[0][j];
+      sm[16 + j] = sacc[1][j];
+    }
+    const uint64_t vh = vis >> (4 * hf);
+    const uint32_t v0 = (uint32_t)vh, v1 = (uint32_t)(vh >> 32);
+    constexpr uint32_t kVisAll = 0x0F0F0F0Fu;  // bits 8(j/4) + j%4, j = 0..15
+    if (__ballot(((v0 & kVisAll) != kVisAll) || ((v1 & kVisAll) != kVisAll))) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int bit = 8 * (j >> 2) + (j & 3);
+        sm[j] = ((v0 >> bit) & 1u) ? sm[j] : -INFINITY;
+        sm[16 + j] = ((v1 >> bit) & 1u) ? sm[16 + j] : -INFINITY;
+      }
+    }
+    float tm = sm[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) tm = fmaxf(tm, sm[j]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+    }
+    // Reference max. A row whose max exceeds its reference by more than
+    // fold_log2 takes a new reference: at once if it has accumulated nothing yet
+    // (reference -inf); otherwise the wavefront folds its accumulator into
+    // the rows' partial-result slots and restarts it from zero (the
+    // accumulator is only ever touched by MFMAs and by memory instructions
+    // that read it straight from the AGPRs, which keeps it there).
+    const bool grow = tm > m_ref + p.fold_log2;
+    if (__ballot(grow)) {
+      if (__ballot(grow && m_ref != -INFINITY)) {
+        // fold: slot = O + slot * 2^(m_slot - m_ref), against m_ref
+        // (a row with nothing accumulated at the last fold has m_slot = -inf
+        // and a zero slot: it adds nothing)
+        const float beta = m_slot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_slot - m_ref);
+        if (folded) add_slots(o, slot0, rows_valid, beta, ln);
+        TVMLA_O_DRAIN(o);
+        if (r < R) {
+#pragma unroll
+          for (int db = 0; db < 16; ++db) store_block(fold_dst + 32 * db, o[db]);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        l_fold = folded ? l_fold * beta + l_part : l_part;
+        l_part = 0.f;
+        m_slot = m_ref;
+        folded = true;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) TVMLA_MFMA_ZERO(o[db], zero8);
+      }
+      m_ref = grow ? tm : m_ref;
+    }
+
+    // ---- value operands. Step n: key step q = n / 16 (keys 16q ..), entry
+    // block db = n % 16. Score register j of block kb in lane half hf holds
+    // key 32kb + 8(j/4) + 4hf + j%4; key step q = 2kb + c takes registers
+    // 8c .. 8c+7, i.e. keys 16q + 8(m/4) + 4hf + m%4 (m = 0..7), so the V^T
+    // operand holds V rows 16q + 4hf + vr .. (lo) and +8 (hi): lane group row
+    // vr = (lane & 15) / 4 reads latent entries 32db + 16 g1 + 4(lane & 3)
+    // .. +3 (g1 = lane bit 4), piece 4db + vpl (vpl = 2 g1 + (lane & 3) / 2)
+    // stored at 16(db / 4) + ((4(db % 4) + vpl) ^ swz(vr + 8x)).
+    const int vr = 4 * lhf + ((ln & 15) >> 2);
+    const int vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
+    const uint32_t vbase = cur_lds + vr * kLatRow + 8 * (ln & 1);
+    auto vaddr_lo = [&](int d4) -> uint32_t { return vbase + ((vt ^ (4 * d4)) << 4); };
+    auto vaddr_hi = [&](int d4) -> uint32_t { return vbase + ((vt ^ (4 * d4) ^ kSwzHi) << 4); };
+    i16x4_t vlo[kVRing], vhi[kVRing];
+    auto vread = [&](auto n_) {
+      constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
+      constexpr int off = 16 * q * kLatRow + 256 * (db / 4);
+      vlo[n % kVRing] = read_tr<off>(vaddr_lo(db % 4));
+      vhi[n % kVRing] = read_tr<off + 8 * kLatRow>(vaddr_hi(db % 4));
+    };
+    const float mu = m_ref == -INFINITY ? 0.f : -m_ref;
+    bf16x8_t pf[4];  // P^T operand of key step q
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[j], scale2, mu));
+      pf[j >> 3][j & 7] = (__bf16)pj;
+      psum += pj;
+    }
+    l_part += psum;
+
+    // ---- O^T += V^T P^T
+    static_for<0, kVRing>([&](auto x_) { vread(x_); });
+    static_for<0, kVSteps>([&](auto n_) {
+      constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
+      constexpr int ahead = 2 * (kVSteps - 1 - n < kVRing - 1 ? kVSteps - 1 - n : kVRing - 1);
+      wait_lgkm2<ahead>(vlo[n % kVRing], vhi[n % kVRing]);
+      if constexpr (db == 0)  // pf[q] is vector-ALU output: two wait states before an MFMA reads it
+        TVMLA_MFMA_O_NOP(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+      else
+        TVMLA_MFMA_O(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+      if constexpr (n + kVRing < kVSteps) vread(Int<n + kVRing>{});
+    });
+  };
+  for (int tile = 0; tile < ntiles; ++tile) {
+    tile_barrier();  // tile in LDS; every wavefront is done with the previous one
+    const bool odd = tile & 1;
+    body(tile, odd ? kb1 : kb0, odd ? kb0 : kb1);
+  }
+  // The last tile's prefetch targeted the idle buffer; let it land before
+  // the workgroup exits and releases its LDS.
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  TVMLA_O_DRAIN(o);
+
+  // The folded part (against m_slot) joins the accumulator (against m_ref).
+  const float beta = folded && m_slot != -INFINITY ? __builtin_amdgcn_exp2f(m_slot - m_ref) : 0.f;
+  if (folded) {
+    add_slots(o, slot0, rows_valid, beta, lane);
+    TVMLA_O_DRAIN(o);
+  }
+  const float lsum = l_fold * beta + l_part;
+  const float l = lsum + __shfl_xor(lsum, 32, 64);
+  if (r >= R) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      float4 v;
+      v.x = o[db][4 * jg + 0] * inv;
+      v.y = o[db][4 * jg + 1] * inv;
+      v.z = o[db][4 * jg + 2] * inv;
+      v.w = o[db][4 * jg + 3] * inv;
+      *reinterpret_cast<float4*>(fold_dst + 32 * db + 8 * jg) = v;
+    }
+  if (hf == 0) p.lse_part[prow] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_split_rows_bf16(const SplitParams& p, hipStream_t stream) {
+  const int R = p.num_draft * p.num_heads;
+  const int groups = (R + kRowsWG - 1) / kRowsWG;
+  const int pairs = p.batch * p.nsplit;
+  const int64_t blocks = (int64_t)8 * ((pairs + 7) / 8) * groups;
+  SplitParams arg = p;
+  int a_groups = groups, a_pairs = pairs;
+  void* args[] = {&arg, &a_groups, &a_pairs};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&split_rows_kernel), dim3((unsigned)blocks), dim3(256), args,
+                         0, stream);
+}
+
+}  // namespace tvmla

@@ -31,6 +31,7 @@ struct SplitParams {
   float* o_part;    // [batch][nsplit][num_draft * num_heads][512]
   float* lse_part;  // [batch][nsplit][num_draft * num_heads]
   const int64_t* qo_indptr;  // null: num_draft tokens per request; else per-request token ranges
+  float fold_log2;           // row-owner kernel: reference-max growth (log2 units) that triggers a fold
 };
 
 struct CombineParams {
@@ -126,6 +127,7 @@ __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32
 hipError_t launch_split_scalar_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_scalar_fp32(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_mfma_bf16(const SplitParams& p, hipStream_t stream);
+hipError_t launch_split_rows_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& c, int dtype, hipStream_t stream);
 hipError_t launch_defrag(const DefragParams& d, int elem_size, hipStream_t stream);
 hipError_t launch_tree_mask(const TreeMaskParams& m, hipStream_t stream);

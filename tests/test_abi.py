@@ -100,13 +100,14 @@ def test_bad_shape(lib, kw):
     assert _call(lib, **kw) == 2
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1), dict(dtype=binding.FP32, algo=binding.ALGO_MFMA)])
+@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1), dict(dtype=binding.FP32, algo=binding.ALGO_MFMA),
+                                dict(dtype=binding.FP32, algo=binding.ALGO_ROWS)])
 def test_bad_dtype(lib, kw):
     assert _call(lib, **kw) == 3
 
 
 def test_bad_algo(lib):
-    assert _call(lib, algo=3) == 7
+    assert _call(lib, algo=4) == 7
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.07, float("inf"), float("nan")])

@@ -15,7 +15,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-MFMA, SCALAR = binding.ALGO_MFMA, binding.ALGO_SCALAR
+MFMA, SCALAR, ROWS = binding.ALGO_MFMA, binding.ALGO_SCALAR, binding.ALGO_ROWS
 
 
 def _oracle(w, pool=None):
@@ -31,7 +31,7 @@ def _oracle_rows(w, picks, pool=None):
 
 
 def _algos(w):
-    return [SCALAR] if w.spec.dtype == "fp32" else [MFMA, SCALAR]
+    return [SCALAR] if w.spec.dtype == "fp32" else [ROWS, MFMA, SCALAR]
 
 
 SMALL = {
@@ -81,9 +81,48 @@ def test_nsplit_invariance(nsplit):
     w = gen.build("p4096")
     ref_out, ref_lse = _oracle(w)
     d = Device(w, nsplit=nsplit)
-    log(f"[p4096] nsplit={nsplit}")
-    out, lse = d.result(algo=MFMA)
-    compare(w, out, lse, ref_out, ref_lse, f"nsplit{nsplit}")
+    for algo in (ROWS, MFMA):
+        log(f"[p4096] nsplit={nsplit} algo={algo}")
+        out, lse = d.result(algo=algo)
+        compare(w, out, lse, ref_out, ref_lse, f"nsplit{nsplit}/algo{algo}")
+
+
+@pytest.mark.parametrize("fold", ["0", "0.5", "3"])
+@pytest.mark.parametrize("name", ["ragged_h8", "groups_h64", "t64_h2", "chain_h16", "t2_h128"])
+def test_rows_fold_path(monkeypatch, fold, name):
+    """The row-owner kernel folds its accumulator into the workspace when a
+    row's max outgrows its reference by more than TVMLA_FOLD_LOG2 (16 by
+    default, rare on these inputs). Thresholds of 0..3 make folds frequent,
+    including repeated folds into the same slot; the result must not
+    change."""
+    w = gen.build(SMALL[name])
+    ref_out, ref_lse = _oracle(w)
+    for ns in (1, 2):  # long splits: folds need tiles after a row's first
+        d = Device(w, nsplit=ns)
+        base_out, base_lse = d.result(algo=ROWS)
+        monkeypatch.setenv("TVMLA_FOLD_LOG2", fold)
+        log(f"[{name}] nsplit {ns} fold threshold {fold}")
+        out, lse = d.result(algo=ROWS)
+        monkeypatch.delenv("TVMLA_FOLD_LOG2")
+        compare(w, out, lse, ref_out, ref_lse, f"{name}/nsplit{ns}/fold{fold}")
+        if fold == "0" and max(w.prefix_lens) + w.num_draft > 2 * 64 * ns:
+            # several tiles per split: the folds changed the rounding
+            assert not np.array_equal(out, base_out), "no fold happened"
+
+
+def test_rows_fold_one_split_long():
+    """One split over 4,112 keys (65 tiles) with a fold on every growth of a
+    row max: many folds per slot."""
+    import os
+    w = gen.build("p4096")
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w, nsplit=1)
+    os.environ["TVMLA_FOLD_LOG2"] = "0"
+    try:
+        out, lse = d.result(algo=ROWS)
+    finally:
+        del os.environ["TVMLA_FOLD_LOG2"]
+    compare(w, out, lse, ref_out, ref_lse, "p4096/nsplit1/fold0")
 
 
 @pytest.mark.parametrize("min_chunk", [16, 256, 100000])
@@ -91,7 +130,7 @@ def test_min_chunk(min_chunk):
     w = gen.build(SMALL["groups_h64"])
     ref_out, ref_lse = _oracle(w)
     d = Device(w)
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         out, lse = d.result(algo=algo, min_chunk=min_chunk)
         compare(w, out, lse, ref_out, ref_lse, f"min_chunk{min_chunk}/algo{algo}")
 
@@ -107,7 +146,7 @@ def test_partials_match_oracle_splits():
                                                 w.num_draft, ns)
     d = Device(w, nsplit=ns)
     T, H = w.num_draft, w.num_heads
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         d.ws.fill_(float("nan"))
         d.result(algo=algo)
         o_ws, l_ws = binding.workspace_views(d.ws, w.batch, T, H, ns)
@@ -159,7 +198,7 @@ def test_combine_entry_point():
 def test_deterministic_and_poison_free():
     w = gen.build(SMALL["groups_h64"])
     d = Device(w)
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         o1, l1 = d.result(algo=algo)
         d.out.fill_(float("nan"))
         d.lse.fill_(float("nan"))
@@ -175,7 +214,7 @@ def test_slot_layout_bitwise():
     b = gen.build(gen.small("lay", 2, [333, 70], 8, 16, seed=21, layout="contiguous"))
     assert not np.array_equal(a.slots, b.slots)
     da, db, dp = Device(a), Device(b), Device(a, row_stride=640)
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         oa, la = da.result(algo=algo)
         ob, lb = db.result(algo=algo)
         op, lp = dp.result(algo=algo)
@@ -190,7 +229,7 @@ def test_masked_content_independence():
     N = P + T
     vis = w.custom_mask.reshape(T, N).numpy() != 0
     leaf = max(range(T), key=lambda j: -vis[:, P + j].sum())  # seen by the fewest tokens
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         o1, l1 = d.result(algo=algo)
         saved = d.pool[int(w.out_cache_loc[leaf])].clone()
         d.pool[int(w.out_cache_loc[leaf])] = 37.0
@@ -233,16 +272,17 @@ def test_full_size_sampled(name, per_request):
     w = gen.build(name)
     log(f"[{name}] built: batch={w.batch} keys={w.total_keys}")
     d = Device(w)
-    out, lse = d.run(algo=binding.ALGO_AUTO)
-    torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    _convex_bounds(d, w, out)
     picks = _picks(w, per_request)
     pool = w.host_pool()
     ref_o, ref_l = _oracle_rows(w, picks, pool)
-    got_o = np.stack([out[t, h].float().cpu().numpy() for t, h in picks]).astype(np.float64)
-    got_l = np.array([float(lse[t, h]) for t, h in picks])
-    compare(w, got_o, got_l, ref_o, ref_l, f"{name} sampled {len(picks)} rows")
+    for algo in (ROWS, binding.ALGO_AUTO):
+        out, lse = d.run(algo=algo)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+        _convex_bounds(d, w, out)
+        got_o = np.stack([out[t, h].float().cpu().numpy() for t, h in picks]).astype(np.float64)
+        got_l = np.array([float(lse[t, h]) for t, h in picks])
+        compare(w, got_o, got_l, ref_o, ref_l, f"{name} algo{algo} sampled {len(picks)} rows")
     if name == "heavy200k":
         c = gen.build("heavy200k_contig")
         dc = Device(c)
@@ -303,7 +343,7 @@ def test_graph_capture_replay():
 def test_partials_then_combine_equals_verify():
     w = gen.build(SMALL["groups_h64"])
     d = Device(w)
-    for algo in (MFMA, SCALAR):
+    for algo in (ROWS, MFMA, SCALAR):
         o1, l1 = d.result(algo=algo)
         d.out.fill_(float("nan"))
         d.lse.fill_(float("nan"))

@@ -46,11 +46,13 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
-@pytest.mark.parametrize("algo", [binding.ALGO_AUTO, binding.ALGO_SCALAR])
+@pytest.mark.parametrize("algo", [binding.ALGO_AUTO, binding.ALGO_ROWS, binding.ALGO_SCALAR])
 def test_ragged_matches_oracle(name, algo):
     kw, tokens = CASES[name]
     w = gen.build(gen.small(name, **kw))
     r = gen.ragged_trees(w, tokens)
+    if algo == binding.ALGO_ROWS and w.spec.dtype == "fp32":
+        pytest.skip("the MFMA kernels take bf16 only")
     log(f"ragged case {name} algo {algo}: tokens {tokens}")
     out, lse = _run(w, r, algo=algo)
     if sum(tokens) == 0:
