@@ -67,12 +67,22 @@ typedef enum {
 } tvmla_status;
 
 typedef enum {
-  TVMLA_ALGO_AUTO = 0,   /* bf16 -> MFMA kernel, fp32 -> scalar kernel          */
+  TVMLA_ALGO_AUTO = 0,   /* bf16 -> ROWS when batch * nsplit * ceil(num_draft *
+                            num_heads / 128) >= 256, else MFMA; fp32 -> SCALAR */
   TVMLA_ALGO_SCALAR = 1, /* one wavefront per (row, split); fp32 FMA; any dtype */
   TVMLA_ALGO_MFMA = 2,   /* bf16 MFMA kernel, 64 query rows per workgroup       */
   TVMLA_ALGO_ROWS = 3    /* bf16 MFMA kernel, 128 query rows per workgroup, each
                             wavefront owning 32 rows outright; bf16 only       */
 } tvmla_algo;
+
+/*
+ * TVMLA_ALGO_ROWS keeps each row's softmax against a reference max and
+ * folds its accumulator into the row's workspace slot when the row's max
+ * outgrows that reference by more than 2^16 (log2 units). The environment
+ * variable TVMLA_FOLD_LOG2 (a number >= 0, read at every call) overrides the
+ * 16; results are the same for any value, only the number of folds changes
+ * (tests use it to exercise the fold path). Other algorithms ignore it.
+ */
 
 /*
  * Bytes of workspace tvmla_verify needs: the per-split partial results

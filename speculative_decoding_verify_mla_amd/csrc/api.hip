@@ -42,6 +42,16 @@ float fold_log2() {
   return 16.f;
 }
 
+// bf16 kernel choice: the 128-row kernel does a third less work per row
+// (staging, barriers and softmax exchange amortised over twice the rows),
+// but launches half the workgroups of the 64-row one; it is taken when its
+// grid still covers the 256 compute units.
+int32_t auto_bf16(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
+  const int64_t rows = (int64_t)num_draft * num_heads;
+  const int64_t wgs = (int64_t)batch * nsplit * ((rows + 127) / 128);
+  return wgs >= 256 ? TVMLA_ALGO_ROWS : TVMLA_ALGO_MFMA;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,7 +91,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
   if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA && algo != TVMLA_ALGO_ROWS)
     return TVMLA_E_ALGO;
-  if (algo == TVMLA_ALGO_AUTO) algo = dtype == TVMLA_BF16 ? TVMLA_ALGO_MFMA : TVMLA_ALGO_SCALAR;
+  if (algo == TVMLA_ALGO_AUTO) algo = dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, nsplit) : TVMLA_ALGO_SCALAR;
   if ((algo == TVMLA_ALGO_MFMA || algo == TVMLA_ALGO_ROWS) && dtype != TVMLA_BF16) return TVMLA_E_DTYPE;
   if (!q_nope || !q_rope || !kv_cache || !kv_indptr || !kv_indices || !out_cache_loc || !custom_mask ||
       !mask_indptr)

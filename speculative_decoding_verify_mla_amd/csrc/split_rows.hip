@@ -238,6 +238,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_rows_kernel(SplitParams p, int groups, int pairs) {
   __shared__ __attribute__((aligned(16))) char kb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char kb1[kTileBytes];
+  // the rope part of the 128 rows' queries (128 bytes per row, pieces
+  // XOR-swizzled by the row): read for the four rope k-steps of each key
+  // block instead of being held in registers for the whole split
+  __shared__ __attribute__((aligned(16))) char qrope[kRowsWG * kRopeRow];
 
   // Workgroup ids reach the 8 XCDs round-robin (id % 8); every row group of
   // one (request, split) pair gets the same id % 8, so the pair's key rows
@@ -278,16 +282,20 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const int h = rr - i * p.num_heads;
   const int64_t t = tb + i;
 
-  // Q^T operands: the lane's row, key entries [16ks + 8hf, +8).
-  bf16x8_t qf[kQSteps];
+  // Q^T operands: the lane's row, key entries [16ks + 8hf, +8): the 32
+  // latent k-steps in registers, the 4 rope k-steps in LDS (rope piece
+  // 2c + hf of local row x at position (2c + hf) ^ (x % 8)).
+  bf16x8_t qf[kDLatent / 16];
   {
     const uint16_t* qn = static_cast<const uint16_t*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head + 8 * hf;
     const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + t * p.qr_stride_tok + h * p.qr_stride_head + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < kDLatent / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qn + 16 * ks));
+    char* qrow = qrope + (32 * wave + col) * kRopeRow;
 #pragma unroll
-    for (int ks = 0; ks < kDRope / 16; ++ks)
-      qf[kDLatent / 16 + ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * ks));
+    for (int c = 0; c < kDRope / 16; ++c)
+      *reinterpret_cast<uint4*>(qrow + (((2 * c + hf) ^ (col & 7)) << 4)) =
+          *reinterpret_cast<const uint4*>(qr + 16 * c);
   }
 
   f32x16_t o[16];  // O^T blocks: latent entries [32db, 32db + 32) x the 32 rows
@@ -394,8 +402,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     // 16(ks / 8) + ((2(ks % 8)) ^ sq), sq = swz(col) ^ hf; rope k-step
     // 32 + c reads rope piece 2c + hf stored at (2c + hf) ^ (col % 8).
     // The eight latent address patterns and two rope ones are registers;
-    // block, piece group and rope block are immediate offsets. The next
-    // tile's sixteen latent loads go one per four MFMAs.
+    // block, piece group and rope block are immediate offsets.
     const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
     const int lcol = ln & 31, lhf = ln >> 5;
     const int sq = piece_swz(lcol) ^ lhf;
@@ -414,90 +421,68 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       constexpr int off = ks < 32 ? kb * 32 * kLatRow + 256 * (ks / 8) : kb * 32 * kRopeRow;
       return read_b128<off>(saddr(n_));
     };
-    bf16x8_t ring[kSRing];
-    static_for<0, kSRing>([&](auto x_) { ring[decltype(x_)::value] = sread(x_); });
-    f32x16_t sacc[2];
-    static_for<0, kSSteps>([&](auto n_) {
-      constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
-      if constexpr (n % 4 == 1 && n / 4 < 16) stage_key(nxt, ra_lo, ra_hi, wave, ln, n / 4);
-      bf16x8_t& kf = ring[n % kSRing];
-      constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
-      wait_lgkm<ahead>(kf);
-      if constexpr (ks == 0)
-        TVMLA_MFMA_S_FIRST(sacc[kb], kf, qf[0]);
-      else
-        TVMLA_MFMA_S(sacc[kb], kf, qf[ks]);
-      if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
-    });
-    stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
-    stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
 
-    // ---- softmax over the tile. Masked scores become -inf (skipped when the
-    // whole wavefront sees every key). sm_scale > 0, so the maximum of the
-    // raw scores times scale2 is the maximum of the scaled scores exactly.
-    TVMLA_S_DRAIN(sacc[0], sacc[1]);
-    float sm[32];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      sm[j] = sacc[0][j];
-      sm[16 + j] = sacc[1][j];
-    }
+    // ---- softmax pieces for key block h (keys 32h .. 32h+31 of the tile).
+    // Score register j of block h in lane half hf holds key 32h + 8(j/4) +
+    // 4hf + j%4. Masked scores become -inf (the whole wavefront seeing every
+    // key of the tile -- the common case -- skips the selects). sm_scale > 0,
+    // so the maximum of the raw scores times scale2 is the maximum of the
+    // scaled scores exactly. Probabilities are taken against the current
+    // reference m_ref (exp2(s * scale2 - m_ref), one fma each; exp2(-inf) =
+    // 0): valid unless the block's max outgrows the reference, which the
+    // caller checks before using them.
     const uint64_t vh = vis >> (4 * hf);
-    const uint32_t v0 = (uint32_t)vh, v1 = (uint32_t)(vh >> 32);
     constexpr uint32_t kVisAll = 0x0F0F0F0Fu;  // bits 8(j/4) + j%4, j = 0..15
-    if (__ballot(((v0 & kVisAll) != kVisAll) || ((v1 & kVisAll) != kVisAll))) {
+    const bool allvis = __ballot((((uint32_t)vh & kVisAll) != kVisAll) || (((uint32_t)(vh >> 32) & kVisAll) != kVisAll)) == 0;
+    float sm[2][16], tmx[2], psum[2];
+    bf16x8_t pf[4];  // P^T operand of key step q = 2h + c
+    auto mask_block = [&](int h) {
+      if (!allvis) {
+        const uint32_t v = (uint32_t)(vh >> (32 * h));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int bit = 8 * (j >> 2) + (j & 3);
-        sm[j] = ((v0 >> bit) & 1u) ? sm[j] : -INFINITY;
-        sm[16 + j] = ((v1 >> bit) & 1u) ? sm[16 + j] : -INFINITY;
+        for (int j = 0; j < 16; ++j) sm[h][j] = ((v >> (8 * (j >> 2) + (j & 3))) & 1u) ? sm[h][j] : -INFINITY;
       }
-    }
-    float tm = sm[0];
-#pragma unroll
-    for (int j = 1; j < 32; ++j) tm = fmaxf(tm, sm[j]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
-      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
-    }
-    // Reference max. A row whose max exceeds its reference by more than
-    // fold_log2 takes a new reference: at once if it has accumulated nothing yet
-    // (reference -inf); otherwise the wavefront folds its accumulator into
-    // the rows' partial-result slots and restarts it from zero (the
-    // accumulator is only ever touched by MFMAs and by memory instructions
-    // that read it straight from the AGPRs, which keeps it there).
-    const bool grow = tm > m_ref + p.fold_log2;
-    if (__ballot(grow)) {
-      if (__ballot(grow && m_ref != -INFINITY)) {
-        // fold: slot = O + slot * 2^(m_slot - m_ref), against m_ref
-        // (a row with nothing accumulated at the last fold has m_slot = -inf
-        // and a zero slot: it adds nothing)
-        const float beta = m_slot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_slot - m_ref);
-        if (folded) add_slots(o, slot0, rows_valid, beta, ln);
-        TVMLA_O_DRAIN(o);
-        if (r < R) {
-#pragma unroll
-          for (int db = 0; db < 16; ++db) store_block(fold_dst + 32 * db, o[db]);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        l_fold = folded ? l_fold * beta + l_part : l_part;
-        l_part = 0.f;
-        m_slot = m_ref;
-        folded = true;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) TVMLA_MFMA_ZERO(o[db], zero8);
+    };
+    // the block's maximum in five pieces (four scores each, then the lane-half swap)
+    auto max_part = [&](int h, int part) {
+      if (part < 4) {
+        const int j = 4 * part;
+        const float m4 = fmaxf(fmaxf(sm[h][j], sm[h][j + 1]), fmaxf(sm[h][j + 2], sm[h][j + 3]));
+        tmx[h] = part == 0 ? m4 : fmaxf(tmx[h], m4);
+      } else {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx[h]), __float_as_uint(tmx[h]), false, false);
+        tmx[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
       }
-      m_ref = grow ? tm : m_ref;
-    }
+    };
+    // probability j of block h against mu = -m_ref (0 while m_ref = -inf);
+    // odd j also packs the pair into the P^T operand
+    float pt[16];
+    auto prob1 = [&](int h, int j, float mu) {
+      pt[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[h][j], scale2, mu));
+      psum[h] = j == 0 ? pt[j] : psum[h] + pt[j];
+      if (j & 1) {
+        pf[2 * h + (j >> 3)][(j & 7) - 1] = (__bf16)pt[j - 1];
+        pf[2 * h + (j >> 3)][j & 7] = (__bf16)pt[j];
+      }
+    };
+    auto probs_block = [&](int h, float mu) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) prob1(h, j, mu);
+    };
+    auto max_block = [&](int h) {
+#pragma unroll
+      for (int part = 0; part < 5; ++part) max_part(h, part);
+    };
+    const float mu0 = m_ref == -INFINITY ? 0.f : -m_ref;
 
-    // ---- value operands. Step n: key step q = n / 16 (keys 16q ..), entry
-    // block db = n % 16. Score register j of block kb in lane half hf holds
-    // key 32kb + 8(j/4) + 4hf + j%4; key step q = 2kb + c takes registers
-    // 8c .. 8c+7, i.e. keys 16q + 8(m/4) + 4hf + m%4 (m = 0..7), so the V^T
-    // operand holds V rows 16q + 4hf + vr .. (lo) and +8 (hi): lane group row
-    // vr = (lane & 15) / 4 reads latent entries 32db + 16 g1 + 4(lane & 3)
-    // .. +3 (g1 = lane bit 4), piece 4db + vpl (vpl = 2 g1 + (lane & 3) / 2)
-    // stored at 16(db / 4) + ((4(db % 4) + vpl) ^ swz(vr + 8x)).
+    // ---- value product O^T += V^T P^T, step n: key step q = n / 16 (keys
+    // 16q ..), entry block db = n % 16. Key step q = 2h + c takes score
+    // registers 8c .. 8c+7 of block h, i.e. keys 16q + 8(m/4) + 4hf + m%4
+    // (m = 0..7), so the V^T operand holds V rows 16q + 4hf + vr .. (lo) and
+    // +8 (hi): lane group row vr = (lane & 15) / 4 reads latent entries
+    // 32db + 16 g1 + 4(lane & 3) .. +3 (g1 = lane bit 4), piece 4db + vpl
+    // (vpl = 2 g1 + (lane & 3) / 2) stored at 16(db / 4) + ((4(db % 4) + vpl)
+    // ^ swz(vr + 8x)).
     const int vr = 4 * lhf + ((ln & 15) >> 2);
     const int vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
     const uint32_t vbase = cur_lds + vr * kLatRow + 8 * (ln & 1);
@@ -510,29 +495,122 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       vlo[n % kVRing] = read_tr<off>(vaddr_lo(db % 4));
       vhi[n % kVRing] = read_tr<off + 8 * kLatRow>(vaddr_hi(db % 4));
     };
-    const float mu = m_ref == -INFINITY ? 0.f : -m_ref;
-    bf16x8_t pf[4];  // P^T operand of key step q
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[j], scale2, mu));
-      pf[j >> 3][j & 7] = (__bf16)pj;
-      psum += pj;
-    }
-    l_part += psum;
+    // value steps [B, E); `side(i)` runs between steps (i = step - B)
+    auto pv_steps = [&](auto b_, auto e_, auto&& side) {
+      constexpr int B = decltype(b_)::value, E = decltype(e_)::value;
+      static_for<B, E>([&](auto n_) {
+        constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
+        constexpr int ahead = 2 * (kVSteps - 1 - n < kVRing - 1 ? kVSteps - 1 - n : kVRing - 1);
+        wait_lgkm2<ahead>(vlo[n % kVRing], vhi[n % kVRing]);
+        if constexpr (db == 0)  // pf[q] is vector-ALU output: two wait states before an MFMA reads it
+          TVMLA_MFMA_O_NOP(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+        else
+          TVMLA_MFMA_O(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+        if constexpr (n + kVRing < kVSteps) vread(Int<n + kVRing>{});
+        side(Int<n - B>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
 
-    // ---- O^T += V^T P^T
-    static_for<0, kVRing>([&](auto x_) { vread(x_); });
-    static_for<0, kVSteps>([&](auto n_) {
-      constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
-      constexpr int ahead = 2 * (kVSteps - 1 - n < kVRing - 1 ? kVSteps - 1 - n : kVRing - 1);
-      wait_lgkm2<ahead>(vlo[n % kVRing], vhi[n % kVRing]);
-      if constexpr (db == 0)  // pf[q] is vector-ALU output: two wait states before an MFMA reads it
-        TVMLA_MFMA_O_NOP(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+    // ---- scores. Block 0's softmax pieces ride along block 1's MFMAs
+    // (from two MFMAs after block 0's last, when its results are written).
+    // The next tile's sixteen latent loads go one per four MFMAs, the rope
+    // loads after the last operand wait.
+    // The rope part of the queries is read from LDS four k-steps before the
+    // block's rope steps, right after that step's operand read, so the
+    // operand wait of the first rope step covers it as well.
+    const uint32_t qrbase = (uint32_t)(uintptr_t)TVMLA_LDS(const char, qrope) + (32 * wave + lcol) * kRopeRow;
+    bf16x8_t ring[kSRing], qrf[kDRope / 16];
+    static_for<0, kSRing>([&](auto x_) { ring[decltype(x_)::value] = sread(x_); });
+    f32x16_t sacc[2];
+    static_for<0, kSSteps>([&](auto n_) {
+      constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
+      if constexpr (n % 4 == 1 && n / 4 < 16) stage_key(nxt, ra_lo, ra_hi, wave, ln, n / 4);
+      bf16x8_t& kf = ring[n % kSRing];
+      constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
+      wait_lgkm<ahead>(kf);
+      if constexpr (ks == 32)  // the rope operands were read before this step's operand (see below)
+        asm volatile("" : "+v"(qrf[0]), "+v"(qrf[1]), "+v"(qrf[2]), "+v"(qrf[3]));
+      if constexpr (ks == 0)
+        TVMLA_MFMA_S_FIRST(sacc[kb], kf, qf[0]);
+      else if constexpr (ks < 32)
+        TVMLA_MFMA_S(sacc[kb], kf, qf[ks]);
       else
-        TVMLA_MFMA_O(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
-      if constexpr (n + kVRing < kVSteps) vread(Int<n + kVRing>{});
+        TVMLA_MFMA_S(sacc[kb], kf, qrf[ks - 32]);
+      if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
+      static_assert(kSRing == 4, "the rope operand reads assume four operand reads in flight");
+      if constexpr (ks == 32 - kSRing) {
+        static_for<0, kDRope / 16>([&](auto c_) {
+          constexpr int c = decltype(c_)::value;
+          qrf[c] = read_b128<0>(qrbase + (((2 * c) ^ rsw) << 4));
+        });
+      }
+      constexpr int i = n - (kQSteps + 2);  // block 0's pieces, about one MFMA's worth each
+      if constexpr (i == 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sm[0][j] = sacc[0][j];
+        mask_block(0);
+      }
+      if constexpr (i >= 1 && i <= 5) max_part(0, i - 1);
+      if constexpr (i >= 6 && i < 22) prob1(0, i - 6, mu0);
+      __builtin_amdgcn_sched_barrier(0);
     });
+    stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
+    stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
+
+    // Reference max. A row whose max exceeds its reference by more than
+    // fold_log2 takes a new reference: at once if it has accumulated nothing
+    // yet (reference -inf); otherwise the wavefront first folds its
+    // accumulator into the rows' partial-result slots and restarts it from
+    // zero (the accumulator is only ever touched by MFMAs and by memory
+    // instructions that read it straight from the AGPRs, which keeps it
+    // there).
+    auto fold = [&]() {
+      // slot = O + slot * 2^(m_slot - m_ref), against m_ref (a row with
+      // nothing accumulated at the last fold has m_slot = -inf and a zero slot)
+      const float beta = m_slot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_slot - m_ref);
+      TVMLA_O_DRAIN(o);
+      if (folded) add_slots(o, slot0, rows_valid, beta, ln);
+      TVMLA_O_DRAIN(o);
+      if (r < R) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db) store_block(fold_dst + 32 * db, o[db]);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      l_fold = folded ? l_fold * beta + l_part : l_part;
+      l_part = 0.f;
+      m_slot = m_ref;
+      folded = true;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) TVMLA_MFMA_ZERO(o[db], zero8);
+    };
+    // Block 1's maximum, once its last MFMA's results are written.
+    asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc[1]));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sm[1][j] = sacc[1][j];
+    mask_block(1);
+    max_block(1);
+    const float tm = fmaxf(tmx[0], tmx[1]);
+    const bool grow = tm > m_ref + p.fold_log2;
+    if (__ballot(grow)) {
+      // A row's max outgrew its reference (always so on the first tile with
+      // a visible key): fold first if that row has accumulated something,
+      // move the reference, redo block 0's probabilities
+      if (__ballot(grow && m_ref != -INFINITY)) fold();
+      m_ref = grow ? tm : m_ref;
+      probs_block(0, m_ref == -INFINITY ? 0.f : -m_ref);
+    }
+    const float mu1 = m_ref == -INFINITY ? 0.f : -m_ref;
+
+    // ---- value steps of block 0 while block 1's probabilities are
+    // computed alongside, then block 1's value steps
+    static_for<0, kVRing>([&](auto x_) { vread(x_); });
+    pv_steps(Int<0>{}, Int<32>{}, [&](auto i_) {
+      constexpr int i = decltype(i_)::value;
+      if constexpr (i >= 1 && i < 17) prob1(1, i - 1, mu1);
+    });
+    l_part += psum[0] + psum[1];
+    pv_steps(Int<32>{}, Int<64>{}, [](auto) {});
   };
   for (int tile = 0; tile < ntiles; ++tile) {
     tile_barrier();  // tile in LDS; every wavefront is done with the previous one
