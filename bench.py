@@ -40,14 +40,18 @@ def algorithmic(w):
     return dict(kv_bytes=kv_bytes, all_bytes=kv_bytes + meta_bytes + q_bytes + out_bytes, flops=flops)
 
 
-def profiled_traffic():
-    """HBM bytes per split launch from the committed rocprofv3 summary, or None
-    if the split kernel's source has changed since those counters were taken."""
+KERNEL_OF_ALGO = {1: "split_scalar", 2: "split_mfma", 3: "split_rows"}
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per split launch of `kernel` (a csrc file stem) from the
+    committed rocprofv3 summary, or None if there is none or the kernel's
+    source has changed since those counters were taken."""
     import hashlib
     import re
 
-    prof = os.path.join(ROOT, "profiles", "split_mfma_long185k.md")
-    src = os.path.join(ROOT, "speculative_decoding_verify_mla_amd", "csrc", "split_mfma.hip")
+    prof = os.path.join(ROOT, "profiles", f"{kernel}_long185k.md")
+    src = os.path.join(ROOT, "speculative_decoding_verify_mla_amd", "csrc", f"{kernel}.hip")
     try:
         text = open(prof).read()
         m = re.search(r"traffic_bytes_per_launch: fetch=(\d+) write=(\d+) source_sha256_prefix=([0-9a-f]+)", text)
@@ -257,6 +261,8 @@ def main(argv=None):
     if args.op == "tree_mask":
         return bench_tree_mask(args, w, torch, binding)
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
+    algo_used = args.algo or binding.auto_algo(w.batch, T, H, args.nsplit or ns, 0 if w.spec.dtype == "bf16" else 1)
+    kernel = KERNEL_OF_ALGO.get(algo_used, "split")
     pool = w.device_pool(dev, fill=0.0)
     kv = pool
     q_nope, q_rope = w.q_nope.to(dev), w.q_rope.to(dev)
@@ -347,14 +353,16 @@ def main(argv=None):
             "num_heads": H,
             "nsplit": ns,
             "min_chunk": args.min_chunk,
+            "algo": algo_used,
             "pool_slots": w.spec.pool_slots,
             "layout": w.spec.layout,
             "kv_bytes": alg["kv_bytes"],
             "flops": alg["flops"],
         },
         "kernels_us": {"split": round(ms_split * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
-        "roofline": dict(roof, kernel="split",
-                         traffic=profiled_traffic() if args.workload == "long185k" and args.min_chunk == 0 else None),
+        "roofline": dict(roof, kernel=kernel,
+                         traffic=profiled_traffic(kernel) if args.workload == "long185k" and args.min_chunk == 0
+                         else None),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)

@@ -290,6 +290,13 @@ const char* tvmla_status_str(int32_t status);
 /* Library version: major*10000 + minor*100 + patch. */
 int32_t tvmla_version(void);
 
+/*
+ * The algorithm TVMLA_ALGO_AUTO resolves to for these sizes and dtype (a
+ * tvmla_algo value), or a negative tvmla_status for out-of-range sizes or
+ * an unknown dtype. Host only; no HIP call.
+ */
+int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit, int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

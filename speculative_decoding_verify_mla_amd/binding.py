@@ -32,7 +32,8 @@ STATUS = {
 
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_ragged", "tvmla_verify_partials",
-           "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version")
+           "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version",
+           "tvmla_auto_algo")
 
 
 class TvmlaError(RuntimeError):
@@ -78,6 +79,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_status_str.restype = ctypes.c_char_p
     lib.tvmla_version.argtypes = []
     lib.tvmla_version.restype = _I32
+    lib.tvmla_auto_algo.argtypes = [_I32] * 5
+    lib.tvmla_auto_algo.restype = _I32
     _lib = lib
     return lib
 
@@ -88,6 +91,11 @@ def status_str(status: int) -> str:
 
 def version() -> int:
     return load().tvmla_version()
+
+
+def auto_algo(batch: int, num_draft: int, num_heads: int, nsplit: int, dtype: int = 0) -> int:
+    """The algorithm ALGO_AUTO resolves to for these sizes (negative status if out of range)."""
+    return load().tvmla_auto_algo(batch, num_draft, num_heads, nsplit, dtype)
 
 
 def workspace_bytes(batch: int, num_draft: int, num_heads: int, nsplit: int) -> int:

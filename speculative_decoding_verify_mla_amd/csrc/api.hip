@@ -78,6 +78,13 @@ const char* tvmla_status_str(int32_t status) {
 
 int32_t tvmla_version(void) { return 100; /* 0.1.0 */ }
 
+int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit, int32_t dtype) {
+  if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return -TVMLA_E_DTYPE;
+  const tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
+  if (st != TVMLA_OK) return -st;
+  return dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, nsplit) : TVMLA_ALGO_SCALAR;
+}
+
 // Host checks and parameter block shared by tvmla_verify_ex and
 // tvmla_verify_partials. `out`/`lse` are only checked when need_out is set.
 static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,

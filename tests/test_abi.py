@@ -46,6 +46,18 @@ def test_version_and_status_strings(lib):
     assert binding.status_str(99) == "unknown status"
 
 
+def test_auto_algo(lib):
+    # 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512 workgroups -> the 128-row kernel
+    assert binding.auto_algo(1, 16, 64, 64) == binding.ALGO_ROWS
+    # 16 tokens x 8 heads: one row group, 64 workgroups -> the 64-row kernel
+    assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_MFMA
+    assert binding.auto_algo(1, 16, 8, 256) == binding.ALGO_ROWS
+    assert binding.auto_algo(4, 16, 8, 64) == binding.ALGO_ROWS
+    assert binding.auto_algo(1, 4, 64, 64, binding.FP32) == binding.ALGO_SCALAR
+    assert binding.auto_algo(0, 4, 64, 64) == -2
+    assert binding.auto_algo(1, 4, 64, 64, 7) == -3
+
+
 def test_workspace_bytes(lib):
     # fp32 partials: 512-wide output + lse per (token, head, split), 256-byte aligned regions
     bs, T, H, ns = 8, 9, 64, 64
