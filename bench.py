@@ -261,7 +261,10 @@ def main(argv=None):
     if args.op == "tree_mask":
         return bench_tree_mask(args, w, torch, binding)
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
-    algo_used = args.algo or binding.auto_algo(w.batch, T, H, args.nsplit or ns, 0 if w.spec.dtype == "bf16" else 1)
+    # the split count the full call runs (raised above ns only when the grid would leave CUs idle);
+    # the split-only and combine-only timings use it too, so they time the same launches as the step
+    ns_eff = binding.effective_nsplit(w.batch, T, H, ns)
+    algo_used = args.algo or binding.auto_algo(w.batch, T, H, ns, 0 if w.spec.dtype == "bf16" else 1)
     kernel = KERNEL_OF_ALGO.get(algo_used, "split")
     pool = w.device_pool(dev, fill=0.0)
     kv = pool
@@ -279,11 +282,11 @@ def main(argv=None):
                        ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
 
     def split_only():
-        binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns,
-                                ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
+        binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale,
+                                ns_eff, ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
 
     def combine_only():
-        binding.combine(ws, kv_indptr, w.batch, T, H, ns, out, lse, min_chunk=args.min_chunk, stream=stream)
+        binding.combine(ws, kv_indptr, w.batch, T, H, ns_eff, out, lse, min_chunk=args.min_chunk, stream=stream)
 
     def timed(fn, k):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -352,6 +355,7 @@ def main(argv=None):
             "num_draft": T,
             "num_heads": H,
             "nsplit": ns,
+            "nsplit_effective": ns_eff,
             "min_chunk": args.min_chunk,
             "algo": algo_used,
             "pool_slots": w.spec.pool_slots,

@@ -68,7 +68,8 @@ typedef enum {
 
 typedef enum {
   TVMLA_ALGO_AUTO = 0,   /* bf16 -> ROWS when batch * nsplit * ceil(num_draft *
-                            num_heads / 128) >= 256, else MFMA; fp32 -> SCALAR */
+                            num_heads / 128) >= 256 (nsplit as effectively used,
+                            see tvmla_effective_nsplit), else MFMA; fp32 -> SCALAR */
   TVMLA_ALGO_SCALAR = 1, /* one wavefront per (row, split); fp32 FMA; any dtype */
   TVMLA_ALGO_MFMA = 2,   /* bf16 MFMA kernel, 64 query rows per workgroup       */
   TVMLA_ALGO_ROWS = 3    /* bf16 MFMA kernel, 128 query rows per workgroup, each
@@ -91,7 +92,11 @@ typedef enum {
  * arguments, never on sequence lengths. Returns 0 for out-of-range
  * arguments.
  *
- * Layout (fp32, each region 256-byte aligned), R = num_draft*num_heads:
+ * The size covers tvmla_effective_nsplit(batch, num_draft, num_heads,
+ * nsplit) splits, the count the split+combine entry points use.
+ *
+ * Layout (fp32, each region 256-byte aligned), R = num_draft*num_heads, for
+ * the nsplit a call uses:
  *   o_part   [batch][nsplit][R][512]  split s's output, normalised by its
  *                                     own softmax sum
  *   lse_part [batch][nsplit][R]       split s's natural-log sum of exp
@@ -123,7 +128,9 @@ size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads
  * nsplit        splits per request: split s covers keys
  *               [s*chunk, min((s+1)*chunk, N_b)), chunk = ceil(N_b/nsplit)
  *               (page 1, "The NSPLIT Calculation"); empty splits return at
- *               once.
+ *               once. The call uses tvmla_effective_nsplit(...) splits: a
+ *               fixed multiple of nsplit when the grid would otherwise
+ *               leave compute units idle.
  * out      [batch*num_draft, num_heads, 512] dtype, contiguous; bf16 output
  *          is rounded to nearest even
  * lse      [batch*num_draft, num_heads] fp32, contiguous: natural log of the
@@ -296,6 +303,19 @@ int32_t tvmla_version(void);
  * an unknown dtype. Host only; no HIP call.
  */
 int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit, int32_t dtype);
+
+/*
+ * The split count the split+combine entry points (tvmla_verify, _ex,
+ * _ragged) actually use for these sizes: nsplit, doubled (up to
+ * TVMLA_MAX_NSPLIT) while batch * nsplit * ceil(num_draft * num_heads / 128)
+ * < 256, i.e. while the requested grid would leave compute units idle (few
+ * rows per request, e.g. 8 heads per GPU). A fixed function of the sizes, so
+ * a captured graph keeps its grid; the workspace size from
+ * tvmla_workspace_bytes accounts for it. tvmla_verify_partials and
+ * tvmla_combine use nsplit exactly as given. Negative tvmla_status for
+ * out-of-range sizes. Host only.
+ */
+int32_t tvmla_effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ STATUS = {
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_ragged", "tvmla_verify_partials",
            "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version",
-           "tvmla_auto_algo")
+           "tvmla_auto_algo", "tvmla_effective_nsplit")
 
 
 class TvmlaError(RuntimeError):
@@ -81,6 +81,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_version.restype = _I32
     lib.tvmla_auto_algo.argtypes = [_I32] * 5
     lib.tvmla_auto_algo.restype = _I32
+    lib.tvmla_effective_nsplit.argtypes = [_I32] * 4
+    lib.tvmla_effective_nsplit.restype = _I32
     _lib = lib
     return lib
 
@@ -91,6 +93,11 @@ def status_str(status: int) -> str:
 
 def version() -> int:
     return load().tvmla_version()
+
+
+def effective_nsplit(batch: int, num_draft: int, num_heads: int, nsplit: int) -> int:
+    """Splits verify() really uses for these sizes (negative status if out of range)."""
+    return load().tvmla_effective_nsplit(batch, num_draft, num_heads, nsplit)
 
 
 def auto_algo(batch: int, num_draft: int, num_heads: int, nsplit: int, dtype: int = 0) -> int:

@@ -42,6 +42,20 @@ float fold_log2() {
   return 16.f;
 }
 
+// Splits the split+combine entry points use: the caller's nsplit doubled
+// (up to TVMLA_MAX_NSPLIT) while the 128-row grid, batch * nsplit * ceil(T*H
+// / 128) workgroups, would not cover the 256 compute units -- the shapes with
+// few rows per request (8 heads per GPU). A function of the sizes only, so
+// the grid stays fixed for graph capture; results equal those at nsplit up
+// to rounding (the LSE merge is exact in real arithmetic).
+int32_t effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
+  if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return nsplit;
+  const int64_t groups = ((int64_t)num_draft * num_heads + 127) / 128;
+  int32_t ns = nsplit;
+  while ((int64_t)batch * ns * groups < 256 && 2 * ns <= TVMLA_MAX_NSPLIT) ns *= 2;
+  return ns;
+}
+
 // bf16 kernel choice: the 128-row kernel does a third less work per row
 // (staging, barriers and softmax exchange amortised over twice the rows),
 // but launches half the workgroups of the 64-row one; it is taken when its
@@ -58,7 +72,7 @@ extern "C" {
 
 size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
   if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return 0;
-  return workspace_layout(batch, num_draft, num_heads, nsplit).total;
+  return workspace_layout(batch, num_draft, num_heads, effective_nsplit(batch, num_draft, num_heads, nsplit)).total;
 }
 
 const char* tvmla_status_str(int32_t status) {
@@ -82,7 +96,14 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return -TVMLA_E_DTYPE;
   const tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
   if (st != TVMLA_OK) return -st;
-  return dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, nsplit) : TVMLA_ALGO_SCALAR;
+  return dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, effective_nsplit(batch, num_draft, num_heads, nsplit))
+                             : TVMLA_ALGO_SCALAR;
+}
+
+int32_t tvmla_effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
+  const tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
+  if (st != TVMLA_OK) return -st;
+  return effective_nsplit(batch, num_draft, num_heads, nsplit);
 }
 
 // Host checks and parameter block shared by tvmla_verify_ex and
@@ -166,6 +187,7 @@ static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, i
                                 int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream, int32_t algo, int32_t min_chunk) {
   SplitParams p;
+  nsplit = effective_nsplit(batch, num_draft, num_heads, nsplit);
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
                             q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
                             custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse,

@@ -49,13 +49,26 @@ def test_version_and_status_strings(lib):
 def test_auto_algo(lib):
     # 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512 workgroups -> the 128-row kernel
     assert binding.auto_algo(1, 16, 64, 64) == binding.ALGO_ROWS
-    # 16 tokens x 8 heads: one row group, 64 workgroups -> the 64-row kernel
-    assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_MFMA
-    assert binding.auto_algo(1, 16, 8, 256) == binding.ALGO_ROWS
+    # 16 tokens x 8 heads: one row group; NSPLIT 64 is raised to 256 splits (256 workgroups)
+    assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_ROWS
     assert binding.auto_algo(4, 16, 8, 64) == binding.ALGO_ROWS
+    # 200 splits cannot double within 256: 200 workgroups of 128 rows -> the 64-row kernel
+    assert binding.auto_algo(1, 16, 8, 200) == binding.ALGO_MFMA
     assert binding.auto_algo(1, 4, 64, 64, binding.FP32) == binding.ALGO_SCALAR
     assert binding.auto_algo(0, 4, 64, 64) == -2
     assert binding.auto_algo(1, 4, 64, 64, 7) == -3
+
+
+def test_effective_nsplit(lib):
+    ens = binding.effective_nsplit
+    assert ens(1, 16, 64, 64) == 64          # 8 row groups x 64 splits = 512 workgroups already
+    assert ens(1, 16, 8, 64) == 256          # one row group: doubled twice
+    assert ens(3, 5, 8, 7) == 112            # 3 x 56 = 168 < 256, 3 x 112 = 336
+    assert ens(1, 1, 1, 64) == 256
+    assert ens(1, 16, 8, 200) == 200         # doubling would pass 256
+    assert ens(0, 1, 1, 1) == -2 and ens(1, 1, 1, 257) == -2
+    # the workspace covers the splits the call uses
+    assert binding.workspace_bytes(1, 16, 8, 64) == binding.workspace_bytes(1, 16, 8, 256)
 
 
 def test_workspace_bytes(lib):
@@ -140,13 +153,14 @@ def test_small_workspace(lib):
 
 def test_combine_errors(lib):
     f = lib.tvmla_combine
-    ws = binding.workspace_bytes(1, 4, 64, 64)
-    assert f(_FAKE, ws, _FAKE, 1, 4, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
-    assert f(_FAKE, ws, _FAKE, 1, 4, 64, 64, 0, 0, None, _FAKE, None) == 1
-    assert f(None, ws, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
-    assert f(_FAKE, ws - 1, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
-    assert f(_FAKE, ws, _FAKE, 0, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 2
-    assert f(_FAKE + 4, ws, _FAKE, 1, 4, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
+    # 16 tokens x 64 heads x 64 splits: 512 workgroups, so the workspace is sized for exactly 64 splits
+    ws = binding.workspace_bytes(1, 16, 64, 64)
+    assert f(_FAKE, ws, _FAKE, 1, 16, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
+    assert f(_FAKE, ws, _FAKE, 1, 16, 64, 64, 0, 0, None, _FAKE, None) == 1
+    assert f(None, ws, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    assert f(_FAKE, ws - 1, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    assert f(_FAKE, ws, _FAKE, 0, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 2
+    assert f(_FAKE + 4, ws, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
@@ -157,8 +171,8 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 def test_partials_errors(lib):
     f = lib.tvmla_verify_partials
-    ws = binding.workspace_bytes(1, 4, 64, 64)
-    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 4, 64, 0.07,
+    ws = binding.workspace_bytes(1, 16, 64, 64)
+    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 16, 64, 0.07,
             64, binding.BF16, _FAKE, ws, None, 0, 0]
     for idx, val, code in [(0, None, 1), (6, None, 1), (19, None, 4), (20, ws - 1, 4), (13, 0, 2), (18, 7, 3),
                            (22, 9, 7), (7, 580, 5), (23, -1, 2)]:

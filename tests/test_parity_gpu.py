@@ -30,6 +30,16 @@ def _oracle_rows(w, picks, pool=None):
                           w.mask_indptr, w.sm_scale, w.num_draft, picks)
 
 
+def _explicit(d, w, ns, algo):
+    """Split step + combine at exactly `ns` splits (the full call may raise a
+    small split count to fill the GPU; see effective_nsplit)."""
+    binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc, d.custom_mask,
+                            d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo)
+    binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, ns, d.out, d.lse)
+    torch.cuda.synchronize()
+    return d.out.float().cpu().numpy().astype(np.float64), d.lse.cpu().numpy().astype(np.float64)
+
+
 def _algos(w):
     return [SCALAR] if w.spec.dtype == "fp32" else [ROWS, MFMA, SCALAR]
 
@@ -83,7 +93,7 @@ def test_nsplit_invariance(nsplit):
     d = Device(w, nsplit=nsplit)
     for algo in (ROWS, MFMA):
         log(f"[p4096] nsplit={nsplit} algo={algo}")
-        out, lse = d.result(algo=algo)
+        out, lse = _explicit(d, w, nsplit, algo)
         compare(w, out, lse, ref_out, ref_lse, f"nsplit{nsplit}/algo{algo}")
 
 
@@ -99,10 +109,10 @@ def test_rows_fold_path(monkeypatch, fold, name):
     ref_out, ref_lse = _oracle(w)
     for ns in (1, 2):  # long splits: folds need tiles after a row's first
         d = Device(w, nsplit=ns)
-        base_out, base_lse = d.result(algo=ROWS)
+        base_out, base_lse = _explicit(d, w, ns, ROWS)
         monkeypatch.setenv("TVMLA_FOLD_LOG2", fold)
         log(f"[{name}] nsplit {ns} fold threshold {fold}")
-        out, lse = d.result(algo=ROWS)
+        out, lse = _explicit(d, w, ns, ROWS)
         monkeypatch.delenv("TVMLA_FOLD_LOG2")
         compare(w, out, lse, ref_out, ref_lse, f"{name}/nsplit{ns}/fold{fold}")
         if fold == "0" and max(w.prefix_lens) + w.num_draft > 2 * 64 * ns:
@@ -119,7 +129,7 @@ def test_rows_fold_one_split_long():
     d = Device(w, nsplit=1)
     os.environ["TVMLA_FOLD_LOG2"] = "0"
     try:
-        out, lse = d.result(algo=ROWS)
+        out, lse = _explicit(d, w, 1, ROWS)
     finally:
         del os.environ["TVMLA_FOLD_LOG2"]
     compare(w, out, lse, ref_out, ref_lse, "p4096/nsplit1/fold0")
@@ -148,7 +158,10 @@ def test_partials_match_oracle_splits():
     T, H = w.num_draft, w.num_heads
     for algo in (ROWS, MFMA, SCALAR):
         d.ws.fill_(float("nan"))
-        d.result(algo=algo)
+        # the split step alone keeps nsplit as given (the full call may raise it; see effective_nsplit)
+        binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
+                                d.custom_mask, d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo)
+        torch.cuda.synchronize()
         o_ws, l_ws = binding.workspace_views(d.ws, w.batch, T, H, ns)
         o_ws, l_ws = o_ws.cpu().numpy().astype(np.float64), l_ws.cpu().numpy().astype(np.float64)
         for b in range(w.batch):
@@ -338,6 +351,27 @@ def test_graph_capture_replay():
             compare(x, go, gl, ro, rl, f"replay{rep}/P={list(x.prefix_lens)}")
             eo, el = d.result()  # eager, same buffers
             assert np.array_equal(go, eo) and np.array_equal(gl, el)
+
+
+def test_effective_nsplit_matches_explicit():
+    """Few rows per request: the full call raises the split count; it is
+    bit-identical to split + combine at that count, and matches the oracle."""
+    w = gen.build(SMALL["ragged_h8"])  # 3 requests x 40 rows
+    ns = 7
+    eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, ns)
+    assert eff == 112
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w, nsplit=ns)
+    for algo in (binding.ALGO_AUTO, ROWS, MFMA):
+        o1, l1 = d.result(algo=algo)
+        compare(w, o1, l1, ref_out, ref_lse, f"ragged_h8/nsplit{ns}->{eff}/algo{algo}")
+        binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
+                                d.custom_mask, d.mask_indptr, w.sm_scale, eff, d.ws, w.num_draft, algo=algo)
+        binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, eff, d.out, d.lse)
+        torch.cuda.synchronize()
+        o2 = d.out.float().cpu().numpy().astype(np.float64)
+        l2 = d.lse.cpu().numpy().astype(np.float64)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_partials_then_combine_equals_verify():
