@@ -95,10 +95,15 @@ typedef enum {
  * The size covers tvmla_effective_nsplit(batch, num_draft, num_heads,
  * nsplit) splits, the count the split+combine entry points use.
  *
- * Layout (fp32, each region 256-byte aligned), R = num_draft*num_heads, for
- * the nsplit a call uses:
- *   o_part   [batch][nsplit][R][512]  split s's output, normalised by its
- *                                     own softmax sum
+ * Layout (each region 256-byte aligned), R = num_draft*num_heads, for the
+ * nsplit a call uses:
+ *   o_part   [batch][nsplit][R] slots of 2 KB: split s's output, normalised
+ *                                     by its own softmax sum -- 512 bf16
+ *                                     (rounded to nearest even) in the
+ *                                     slot's first 1 KB for bf16 queries,
+ *                                     512 fp32 for fp32 queries (the
+ *                                     128-row kernel also uses the whole
+ *                                     slot as fp32 scratch while it runs)
  *   lse_part [batch][nsplit][R]       split s's natural-log sum of exp
  *                                     (-inf when the split sees no key)
  * Row r = i*num_heads + h. Only splits that hold keys are written; the

@@ -228,9 +228,10 @@ def combine(workspace, kv_indptr, batch: int, num_draft: int, num_heads: int, ns
     _check(st)
 
 
-def workspace_views(workspace, batch: int, num_draft: int, num_heads: int, nsplit: int):
-    """The partial-result regions of a workspace as tensors:
-    o_part [batch, nsplit, R, 512] and lse_part [batch, nsplit, R] (fp32)."""
+def workspace_views(workspace, batch: int, num_draft: int, num_heads: int, nsplit: int, dtype: int = FP32):
+    """The partial-result regions of a workspace as tensors: o_part [batch,
+    nsplit, R, 512] (bf16 for dtype BF16: the first half of each 2 KB slot;
+    fp32 for FP32) and lse_part [batch, nsplit, R] (fp32)."""
     import torch
 
     R = num_draft * num_heads
@@ -238,7 +239,10 @@ def workspace_views(workspace, batch: int, num_draft: int, num_heads: int, nspli
     o_bytes = rows * D_LATENT * 4
     lse_off = (o_bytes + 255) // 256 * 256
     raw = workspace.view(torch.uint8)
-    o = raw[:o_bytes].view(torch.float32).view(batch, nsplit, R, D_LATENT)
+    if dtype == BF16:
+        o = raw[:o_bytes].view(torch.bfloat16).view(batch, nsplit, R, 2 * D_LATENT)[..., :D_LATENT]
+    else:
+        o = raw[:o_bytes].view(torch.float32).view(batch, nsplit, R, D_LATENT)
     lse = raw[lse_off:lse_off + rows * 4].view(torch.float32).view(batch, nsplit, R)
     return o, lse
 

@@ -14,9 +14,9 @@
 // split maximum and weight sum are reductions over the lse_s (one split per
 // lane of the row's wavefronts); wavefront w of the row then accumulates the
 // weighted partial rows of splits s = w, w+W, w+2W, ... (lane l owns entries
-// [8l, 8l+8); four or eight 2 KB rows in flight per wavefront), and for W > 1 the
-// accumulators are added through LDS. Reads are contiguous 2 KB segments
-// (HBM-bound).
+// [8l, 8l+8); four or eight partial rows in flight per wavefront), and for W > 1
+// the accumulators are added through LDS. A partial row is 1 KB of bf16 (bf16
+// queries) or 2 KB of fp32 (fp32 queries), read contiguously (HBM-bound).
 
 #include "tvmla_internal.h"
 
@@ -40,7 +40,8 @@ __device__ inline float wave_sum(float x) {
 template <bool kBf16, int W>
 __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombineParams c) {
   constexpr int kRowsWG = W >= 4 ? 1 : 4 / W;
-  constexpr int kUnroll = W == 1 ? 4 : 8;  // partial rows in flight per wavefront
+  // partial rows in flight per wavefront (bf16 rows are half the bytes: twice as many)
+  constexpr int kUnroll = (W == 1 ? 4 : 8) * (kBf16 ? 2 : 1);
   __shared__ float red_m[kRowsWG * W], red_l[kRowsWG * W];
   __shared__ __attribute__((aligned(16))) float red_o[W > 1 ? W - 1 : 1][kDLatent];
   const int wave = threadIdx.x >> 6;
@@ -84,8 +85,19 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
     auto add = [&](int s) {
       const size_t pr = base + (size_t)s * R;
       const float w = exp2f((c.lse_part[pr] - mx) * kLog2e);
-      const float4* src = reinterpret_cast<const float4*>(c.o_part + pr * kDLatent + 8 * lane);
-      const float4 a = src[0], d = src[1];
+      float4 a, d;
+      if (kBf16) {  // bf16 partial rows: the slot's first 1 KB
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.o_part + pr * kDLatent) +
+                                                       8 * lane);
+        a = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                        __uint_as_float(u.y & 0xffff0000u));
+        d = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u), __uint_as_float(u.w << 16),
+                        __uint_as_float(u.w & 0xffff0000u));
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(c.o_part + pr * kDLatent + 8 * lane);
+        a = src[0];
+        d = src[1];
+      }
       if (w > 0.f) {  // a split whose row saw no visible key (lse_s = -inf) weighs nothing
         acc[0] = fmaf(w, a.x, acc[0]); acc[1] = fmaf(w, a.y, acc[1]);
         acc[2] = fmaf(w, a.z, acc[2]); acc[3] = fmaf(w, a.w, acc[3]);

@@ -582,19 +582,15 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
     const int row = g * kRowsWG + 32 * x + col;
     if (row >= R) return;
     const size_t prow = ((size_t)b * p.nsplit + s) * Rw + row;
-    float* dst = p.o_part + prow * kDLatent + 128 * wave + 4 * hf;
+    uint16_t* dst = partial_bf16(p.o_part, prow) + 128 * wave + 4 * hf;  // bf16 in the slot's first 1 KB
     const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        float4 v;
-        v.x = ox[db][4 * jg + 0] * inv;
-        v.y = ox[db][4 * jg + 1] * inv;
-        v.z = ox[db][4 * jg + 2] * inv;
-        v.w = ox[db][4 * jg + 3] * inv;
-        *reinterpret_cast<float4*>(dst + 32 * db + 8 * jg) = v;
-      }
+      for (int jg = 0; jg < 4; ++jg)
+        *reinterpret_cast<uint2*>(dst + 32 * db + 8 * jg) =
+            pack_bf16x4(ox[db][4 * jg + 0] * inv, ox[db][4 * jg + 1] * inv, ox[db][4 * jg + 2] * inv,
+                        ox[db][4 * jg + 3] * inv);
     if (wave == 0 && hf == 0) p.lse_part[prow] = lrow > 0.f ? (mref + log2f(lrow)) * kLn2 : -INFINITY;
   };
   write_block(o[0], m_ref0, lrow0, 0);

@@ -632,17 +632,14 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const float l = lsum + __shfl_xor(lsum, 32, 64);
   if (r >= R) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* dst = partial_bf16(p.o_part, prow) + 4 * hf;  // the row's output as bf16 (the slot's first 1 KB)
 #pragma unroll
   for (int db = 0; db < 16; ++db)
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      float4 v;
-      v.x = o[db][4 * jg + 0] * inv;
-      v.y = o[db][4 * jg + 1] * inv;
-      v.z = o[db][4 * jg + 2] * inv;
-      v.w = o[db][4 * jg + 3] * inv;
-      *reinterpret_cast<float4*>(fold_dst + 32 * db + 8 * jg) = v;
-    }
+    for (int jg = 0; jg < 4; ++jg)
+      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * jg) =
+          pack_bf16x4(o[db][4 * jg + 0] * inv, o[db][4 * jg + 1] * inv, o[db][4 * jg + 2] * inv,
+                      o[db][4 * jg + 3] * inv);
   if (hf == 0) p.lse_part[prow] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 

@@ -118,13 +118,20 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(SplitParams p) {
   }
 
   const size_t prow = ((size_t)b * p.nsplit + s) * Rw + r;
-  float* dst = p.o_part + prow * kDLatent + 8 * lane;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float4 a, c;
-  a.x = o[0] * inv; a.y = o[1] * inv; a.z = o[2] * inv; a.w = o[3] * inv;
-  c.x = o[4] * inv; c.y = o[5] * inv; c.z = o[6] * inv; c.w = o[7] * inv;
-  reinterpret_cast<float4*>(dst)[0] = a;
-  reinterpret_cast<float4*>(dst)[1] = c;
+  if (sizeof(T) == 2) {  // bf16 queries: the row as bf16 in the slot's first 1 KB
+    uint16_t* dst = partial_bf16(p.o_part, prow) + 8 * lane;
+    const uint2 a = pack_bf16x4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    const uint2 c = pack_bf16x4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, c.x, c.y);
+  } else {
+    float* dst = p.o_part + prow * kDLatent + 8 * lane;
+    float4 a, c;
+    a.x = o[0] * inv; a.y = o[1] * inv; a.z = o[2] * inv; a.w = o[3] * inv;
+    c.x = o[4] * inv; c.y = o[5] * inv; c.z = o[6] * inv; c.w = o[7] * inv;
+    reinterpret_cast<float4*>(dst)[0] = a;
+    reinterpret_cast<float4*>(dst)[1] = c;
+  }
   if (lane == 0) p.lse_part[prow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 

@@ -123,6 +123,22 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// Four fp32 values as bf16 (round to nearest even), packed into 8 bytes.
+__device__ inline uint2 pack_bf16x4(float a, float b, float c, float d) {
+  uint2 u;
+  u.x = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  u.y = (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16);
+  return u;
+}
+
+// A split's partial output row in the workspace: a 2 KB slot (512 fp32). With
+// bf16 queries the split kernels store the row as 512 bf16 in the slot's
+// first 1 KB (half the bytes to write and to read back in the combine); with
+// fp32 queries as 512 fp32.
+__device__ inline uint16_t* partial_bf16(float* o_part, size_t prow) {
+  return reinterpret_cast<uint16_t*>(o_part + prow * kDLatent);
+}
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_split_scalar_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_split_scalar_fp32(const SplitParams& p, hipStream_t stream);

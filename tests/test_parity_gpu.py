@@ -162,8 +162,8 @@ def test_partials_match_oracle_splits():
         binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
                                 d.custom_mask, d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo)
         torch.cuda.synchronize()
-        o_ws, l_ws = binding.workspace_views(d.ws, w.batch, T, H, ns)
-        o_ws, l_ws = o_ws.cpu().numpy().astype(np.float64), l_ws.cpu().numpy().astype(np.float64)
+        o_ws, l_ws = binding.workspace_views(d.ws, w.batch, T, H, ns, binding.BF16)
+        o_ws, l_ws = o_ws.float().cpu().numpy().astype(np.float64), l_ws.cpu().numpy().astype(np.float64)
         for b in range(w.batch):
             for s in range(ns):
                 got_o = o_ws[b, s].reshape(T, H, 512)
@@ -180,21 +180,24 @@ def test_partials_match_oracle_splits():
 
 
 def test_combine_entry_point():
-    """tvmla_combine on synthetic partials (some splits at -inf, one row all -inf)."""
+    """tvmla_combine on synthetic partials (some splits at -inf, one row all -inf),
+    fp32 partials for an fp32 output and bf16 partials for a bf16 output."""
     batch, T, H, ns = 2, 3, 4, 5
     g = torch.Generator().manual_seed(3)
     nbytes = binding.workspace_bytes(batch, T, H, ns)
-    ws = torch.zeros(nbytes // 4, dtype=torch.float32)
-    o_v, l_v = binding.workspace_views(ws, batch, T, H, ns)
-    o_v.copy_(torch.randn(o_v.shape, generator=g))
-    l_v.copy_(torch.randn(l_v.shape, generator=g) * 3)
-    l_v[0, 1] = float("-inf")
-    l_v[1, :, 5] = float("-inf")
-    o_ref = o_v.permute(0, 2, 1, 3).reshape(batch * T, H, ns, 512).numpy()
-    l_ref = l_v.permute(0, 2, 1).reshape(batch * T, H, ns).numpy()
-    ref_out, ref_lse = vo.combine(o_ref, l_ref)
-    wsd = ws.cuda()
-    for dt, tol in ((torch.float32, 1e-5), (torch.bfloat16, 1e-2)):
+    o_src = torch.randn((batch, ns, T * H, 512), generator=g)
+    l_src = torch.randn((batch, ns, T * H), generator=g) * 3
+    l_src[0, 1] = float("-inf")
+    l_src[1, :, 5] = float("-inf")
+    for dt, code, tol in ((torch.float32, binding.FP32, 1e-5), (torch.bfloat16, binding.BF16, 1e-2)):
+        ws = torch.zeros(nbytes // 4, dtype=torch.float32)
+        o_v, l_v = binding.workspace_views(ws, batch, T, H, ns, code)
+        o_v.copy_(o_src.to(o_v.dtype))
+        l_v.copy_(l_src)
+        o_ref = o_v.float().permute(0, 2, 1, 3).reshape(batch * T, H, ns, 512).numpy()
+        l_ref = l_v.permute(0, 2, 1).reshape(batch * T, H, ns).numpy()
+        ref_out, ref_lse = vo.combine(o_ref, l_ref)
+        wsd = ws.cuda()
         out = torch.full((batch * T, H, 512), float("nan"), dtype=dt, device="cuda")
         lse = torch.full((batch * T, H), float("nan"), device="cuda")
         binding.combine(wsd, None, batch, T, H, ns, out, lse)
