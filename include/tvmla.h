@@ -92,8 +92,9 @@ typedef enum {
  * arguments, never on sequence lengths. Returns 0 for out-of-range
  * arguments.
  *
- * The size covers tvmla_effective_nsplit(batch, num_draft, num_heads,
- * nsplit) splits, the count the split+combine entry points use.
+ * The size covers both nsplit splits (the count tvmla_verify_partials and
+ * tvmla_combine take as given) and tvmla_effective_nsplit(batch, num_draft,
+ * num_heads, nsplit) splits (the count the split+combine entry points use).
  *
  * Layout (each region 256-byte aligned), R = num_draft*num_heads, for the
  * nsplit a call uses:
@@ -311,14 +312,17 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
 
 /*
  * The split count the split+combine entry points (tvmla_verify, _ex,
- * _ragged) actually use for these sizes: nsplit, doubled (up to
- * TVMLA_MAX_NSPLIT) while batch * nsplit * ceil(num_draft * num_heads / 128)
- * < 256, i.e. while the requested grid would leave compute units idle (few
- * rows per request, e.g. 8 heads per GPU). A fixed function of the sizes, so
- * a captured graph keeps its grid; the workspace size from
- * tvmla_workspace_bytes accounts for it. tvmla_verify_partials and
- * tvmla_combine use nsplit exactly as given. Negative tvmla_status for
- * out-of-range sizes. Host only.
+ * _ragged) actually use for these sizes. With G = batch * nsplit *
+ * ceil(num_draft * num_heads / 128) workgroups of the 128-row kernel:
+ * nsplit doubled (up to TVMLA_MAX_NSPLIT) while G < 256, i.e. while the
+ * requested grid would leave compute units idle (few rows per request, e.g.
+ * 8 heads per GPU); else nsplit / 2 when nsplit is even, 256 < G <= 512 and
+ * G / 2 >= 256 (one round of longer splits instead of two rounds, each
+ * workgroup paying its fixed cost before and after the key loop once);
+ * else nsplit. A fixed function of the sizes, so a captured graph keeps its
+ * grid; the workspace size from tvmla_workspace_bytes accounts for it.
+ * tvmla_verify_partials and tvmla_combine use nsplit exactly as given.
+ * Negative tvmla_status for out-of-range sizes. Host only.
  */
 int32_t tvmla_effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit);
 

@@ -122,14 +122,6 @@ __device__ __forceinline__ i16x4_t read_tr(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(Off));
   return r;
 }
-template <int N>
-__device__ __forceinline__ void wait_lgkm(bf16x8_t& r) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm2(i16x4_t& a, i16x4_t& b) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
-}
 
 // Score MFMA (accumulator in VGPRs, read by the softmax) and value MFMA
 // (accumulator in AGPRs). Inline asm keeps the operands where they are; the
@@ -137,12 +129,24 @@ __device__ __forceinline__ void wait_lgkm2(i16x4_t& a, i16x4_t& b) {
 // TVMLA_S_DRAIN before vector code reads a score (24 wait states, twice
 // what 8 passes need), and "s_nop 1" (2 wait states) in front of an MFMA
 // whose operand may have just been written by a vector ALU instruction.
-#define TVMLA_MFMA_S_FIRST(acc, a, q) \
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(q))
-#define TVMLA_MFMA_S(acc, a, q) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q))
-#define TVMLA_MFMA_O(acc, a, p) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p))
-#define TVMLA_MFMA_O_NOP(acc, a, p) \
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p))
+//
+// The operand MFMAs wait for their LDS operand in the same statement
+// ("s_waitcnt lgkmcnt(n)": at most n LDS operations of this wavefront still
+// outstanding). A separate wait statement would have to name the operand
+// as an output, and the compiler then guards every MFMA behind it with a
+// hazard nop as if a vector ALU instruction had just written the operand.
+#define TVMLA_MFMA_S_FIRST(n, acc, a, q)                                                             \
+  asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) \
+               : "v"(a), "v"(q), "n"(n))
+#define TVMLA_MFMA_S(n, acc, a, q)                                                                            \
+  asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q), \
+               "n"(n))
+#define TVMLA_MFMA_O(n, acc, a, p)                                                                            \
+  asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p), \
+               "n"(n))
+#define TVMLA_MFMA_O_NOP(n, acc, a, p)                                                                        \
+  asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc)       \
+               : "v"(a), "v"(p), "n"(n))
 #define TVMLA_MFMA_ZERO(acc, z) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z))
 #define TVMLA_S_DRAIN(s0, s1) asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s0), "+v"(s1))
 #define TVMLA_O_DRAIN(o)                                                                                          \
@@ -194,6 +198,14 @@ __device__ __forceinline__ void add_slots(f32x16_t (&o)[16], const float* slot0,
     }
     asm volatile("" ::: "memory");  // one block's loads at a time
   }
+}
+
+// max(a, b, c) in one instruction. fmaxf on values the compiler cannot
+// prove canonical costs a canonicalizing max per operand besides the max.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // An opaque copy of a value: addresses derived from it are computed where
@@ -443,12 +455,16 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         for (int j = 0; j < 16; ++j) sm[h][j] = ((v >> (8 * (j >> 2) + (j & 3))) & 1u) ? sm[h][j] : -INFINITY;
       }
     };
-    // the block's maximum in five pieces (four scores each, then the lane-half swap)
+    // the block's maximum in five pieces (scores 0..4, 5..8, 9..12, 13..15,
+    // then the lane-half swap)
     auto max_part = [&](int h, int part) {
-      if (part < 4) {
-        const int j = 4 * part;
-        const float m4 = fmaxf(fmaxf(sm[h][j], sm[h][j + 1]), fmaxf(sm[h][j + 2], sm[h][j + 3]));
-        tmx[h] = part == 0 ? m4 : fmaxf(tmx[h], m4);
+      if (part == 0) {
+        tmx[h] = max3(sm[h][0], sm[h][1], sm[h][2]);
+        tmx[h] = max3(tmx[h], sm[h][3], sm[h][4]);
+      } else if (part < 4) {
+        const int j = 4 * part + 1;
+        tmx[h] = max3(tmx[h], sm[h][j], sm[h][j + 1]);
+        tmx[h] = max3(tmx[h], sm[h][j + 2], sm[h][min(j + 3, 15)]);
       } else {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx[h]), __float_as_uint(tmx[h]), false, false);
         tmx[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
@@ -501,11 +517,10 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       static_for<B, E>([&](auto n_) {
         constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
         constexpr int ahead = 2 * (kVSteps - 1 - n < kVRing - 1 ? kVSteps - 1 - n : kVRing - 1);
-        wait_lgkm2<ahead>(vlo[n % kVRing], vhi[n % kVRing]);
         if constexpr (db == 0)  // pf[q] is vector-ALU output: two wait states before an MFMA reads it
-          TVMLA_MFMA_O_NOP(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+          TVMLA_MFMA_O_NOP(ahead, o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
         else
-          TVMLA_MFMA_O(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+          TVMLA_MFMA_O(ahead, o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
         if constexpr (n + kVRing < kVSteps) vread(Int<n + kVRing>{});
         side(Int<n - B>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -528,15 +543,14 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       if constexpr (n % 4 == 1 && n / 4 < 16) stage_key(nxt, ra_lo, ra_hi, wave, ln, n / 4);
       bf16x8_t& kf = ring[n % kSRing];
       constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
-      wait_lgkm<ahead>(kf);
-      if constexpr (ks == 32)  // the rope operands were read before this step's operand (see below)
-        asm volatile("" : "+v"(qrf[0]), "+v"(qrf[1]), "+v"(qrf[2]), "+v"(qrf[3]));
+      // (the rope operands were read right after step 28's operand read, so
+      // step 32's wait covers them too)
       if constexpr (ks == 0)
-        TVMLA_MFMA_S_FIRST(sacc[kb], kf, qf[0]);
+        TVMLA_MFMA_S_FIRST(ahead, sacc[kb], kf, qf[0]);
       else if constexpr (ks < 32)
-        TVMLA_MFMA_S(sacc[kb], kf, qf[ks]);
+        TVMLA_MFMA_S(ahead, sacc[kb], kf, qf[ks]);
       else
-        TVMLA_MFMA_S(sacc[kb], kf, qrf[ks - 32]);
+        TVMLA_MFMA_S(ahead, sacc[kb], kf, qrf[ks - 32]);
       if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
       static_assert(kSRing == 4, "the rope operand reads assume four operand reads in flight");
       if constexpr (ks == 32 - kSRing) {
@@ -553,6 +567,10 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       }
       if constexpr (i >= 1 && i <= 5) max_part(0, i - 1);
       if constexpr (i >= 6 && i < 22) prob1(0, i - 6, mu0);
+      // Keep them here: the reference decision below recomputes them when
+      // the reference moves, and the compiler would otherwise sink them into
+      // the other branch, after the last score MFMA.
+      if constexpr (i == 21) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
       __builtin_amdgcn_sched_barrier(0);
     });
     stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);

@@ -47,7 +47,8 @@ def test_version_and_status_strings(lib):
 
 
 def test_auto_algo(lib):
-    # 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512 workgroups -> the 128-row kernel
+    # 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512 workgroups, run as 32 splits (one round
+    # of 256) -> the 128-row kernel
     assert binding.auto_algo(1, 16, 64, 64) == binding.ALGO_ROWS
     # 16 tokens x 8 heads: one row group; NSPLIT 64 is raised to 256 splits (256 workgroups)
     assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_ROWS
@@ -61,7 +62,11 @@ def test_auto_algo(lib):
 
 def test_effective_nsplit(lib):
     ens = binding.effective_nsplit
-    assert ens(1, 16, 64, 64) == 64          # 8 row groups x 64 splits = 512 workgroups already
+    assert ens(1, 16, 64, 64) == 32          # 8 row groups x 64 splits = 512 workgroups: one round of 256 instead
+    assert ens(1, 16, 64, 63) == 63          # 504 workgroups, odd count: kept
+    assert ens(1, 16, 64, 48) == 48          # 384 workgroups: halving would leave CUs idle
+    assert ens(1, 16, 64, 32) == 32          # exactly one round
+    assert ens(2, 16, 64, 64) == 64          # 1024 workgroups: many rounds, kept
     assert ens(1, 16, 8, 64) == 256          # one row group: doubled twice
     assert ens(3, 5, 8, 7) == 112            # 3 x 56 = 168 < 256, 3 x 112 = 336
     assert ens(1, 1, 1, 64) == 256
@@ -69,6 +74,8 @@ def test_effective_nsplit(lib):
     assert ens(0, 1, 1, 1) == -2 and ens(1, 1, 1, 257) == -2
     # the workspace covers the splits the call uses
     assert binding.workspace_bytes(1, 16, 8, 64) == binding.workspace_bytes(1, 16, 8, 256)
+    # ... and the caller's count, which the split step alone and the combine take as given
+    assert binding.workspace_bytes(1, 16, 64, 64) == binding.workspace_bytes(2, 16, 64, 32)
 
 
 def test_workspace_bytes(lib):
@@ -153,14 +160,14 @@ def test_small_workspace(lib):
 
 def test_combine_errors(lib):
     f = lib.tvmla_combine
-    # 16 tokens x 64 heads x 64 splits: 512 workgroups, so the workspace is sized for exactly 64 splits
-    ws = binding.workspace_bytes(1, 16, 64, 64)
-    assert f(_FAKE, ws, _FAKE, 1, 16, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
-    assert f(_FAKE, ws, _FAKE, 1, 16, 64, 64, 0, 0, None, _FAKE, None) == 1
-    assert f(None, ws, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
-    assert f(_FAKE, ws - 1, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    # 2 requests x 16 tokens x 64 heads x 64 splits: 1024 workgroups, so the workspace is sized for exactly 64 splits
+    ws = binding.workspace_bytes(2, 16, 64, 64)
+    assert f(_FAKE, ws, _FAKE, 2, 16, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
+    assert f(_FAKE, ws, _FAKE, 2, 16, 64, 64, 0, 0, None, _FAKE, None) == 1
+    assert f(None, ws, _FAKE, 2, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
+    assert f(_FAKE, ws - 1, _FAKE, 2, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 4
     assert f(_FAKE, ws, _FAKE, 0, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 2
-    assert f(_FAKE + 4, ws, _FAKE, 1, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
+    assert f(_FAKE + 4, ws, _FAKE, 2, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
@@ -171,8 +178,8 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 def test_partials_errors(lib):
     f = lib.tvmla_verify_partials
-    ws = binding.workspace_bytes(1, 16, 64, 64)
-    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 16, 64, 0.07,
+    ws = binding.workspace_bytes(2, 16, 64, 64)
+    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 16, 64, 0.07,
             64, binding.BF16, _FAKE, ws, None, 0, 0]
     for idx, val, code in [(0, None, 1), (6, None, 1), (19, None, 4), (20, ws - 1, 4), (13, 0, 2), (18, 7, 3),
                            (22, 9, 7), (7, 580, 5), (23, -1, 2)]:

@@ -356,18 +356,21 @@ def test_graph_capture_replay():
             assert np.array_equal(go, eo) and np.array_equal(gl, el)
 
 
-def test_effective_nsplit_matches_explicit():
-    """Few rows per request: the full call raises the split count; it is
-    bit-identical to split + combine at that count, and matches the oracle."""
-    w = gen.build(SMALL["ragged_h8"])  # 3 requests x 40 rows
-    ns = 7
+@pytest.mark.parametrize("name,ns,eff_expected", [
+    ("ragged_h8", 7, 112),   # 3 requests x 40 rows: 21 workgroups, raised to 336
+    ("groups_h64", 32, 16),  # 2 requests x 8 row groups: 512 workgroups, lowered to one round of 256
+])
+def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
+    """The full call runs the effective split count; it is bit-identical to
+    split + combine at that count, and matches the oracle."""
+    w = gen.build(SMALL[name])
     eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, ns)
-    assert eff == 112
+    assert eff == eff_expected
     ref_out, ref_lse = _oracle(w)
     d = Device(w, nsplit=ns)
     for algo in (binding.ALGO_AUTO, ROWS, MFMA):
         o1, l1 = d.result(algo=algo)
-        compare(w, o1, l1, ref_out, ref_lse, f"ragged_h8/nsplit{ns}->{eff}/algo{algo}")
+        compare(w, o1, l1, ref_out, ref_lse, f"{name}/nsplit{ns}->{eff}/algo{algo}")
         binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
                                 d.custom_mask, d.mask_indptr, w.sm_scale, eff, d.ws, w.num_draft, algo=algo)
         binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, eff, d.out, d.lse)
