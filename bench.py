@@ -7,7 +7,16 @@ whole synthetic batch, inputs resident in HBM. Prints ONE JSON line:
 value = effective KV-read GB/s (cache-row bytes the call must read / time per
 call), plus us per call, the split kernel's MFMA roofline fraction (timed
 live with HIP events through tvmla_verify_partials on the same stream), and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+the fp64 CPU oracle timed on a bounded sample of the same workload. The line
+also carries the call captured in a HIP graph and replayed warm and cold
+(L2 and MALL flushed before each replay), and the HBM copy bandwidth and
+bf16 MFMA rate measured on the same GPU.
+
+    python bench.py --report
+
+instead prints one diagnostic line per synthetic configuration (us per call
+eager and graph-replayed warm/cold, KV-read GB/s and share of HBM peak, MFMA
+share, roofline fraction max(t_HBM, t_MFMA) / t).
 """
 from __future__ import annotations
 
@@ -24,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "us per verify call + effective KV-read GB/s (% HBM peak) at 185k ctx"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector ALU, TFLOP/s
 FLOP_PER_ROW_KEY = 2 * 576 + 2 * 512  # QK over the 576-wide key + PV over the 512-wide latent
 
 
@@ -41,6 +51,100 @@ def algorithmic(w):
 
 
 KERNEL_OF_ALGO = {1: "split_scalar", 2: "split_mfma", 3: "split_rows"}
+REPORT_WORKLOADS = ["tiny", "p4096", "long185k", "ragged32", "heavy200k", "heavy200k_contig", "long185k_h8"]
+GRAPH_REPLAYS = 200
+FLUSH_BYTES = 1 << 30  # a 1 GiB write evicts the 4 MB L2s and the 256 MB MALL
+
+
+def _stats_us(ms_list):
+    import numpy as np
+
+    a = np.asarray(ms_list) * 1e3
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def graph_timing(torch, call_on, replays=GRAPH_REPLAYS):
+    """Capture one call (call_on(stream) launches it on `stream`) in a HIP
+    graph, then time `replays` replays, each bracketed by its own events:
+    warm (back to back, the working set partly cached) and cold (an untimed
+    1 GiB write before each replay). Returns µs statistics of both."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call_on(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call_on(side)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("warm", "cold"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        for i, (e0, e1) in enumerate(evs):
+            if mode == "cold":
+                scratch.fill_(i & 0xFF)
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+        torch.cuda.synchronize()
+        res[mode] = _stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    res["replays"] = replays
+    del g, scratch
+    return res
+
+
+def measured_peaks(torch):
+    """HBM bandwidth of a plain 1 GiB device copy (read + write bytes) and
+    the bf16 MFMA rate of the throughput probe, on this GPU."""
+    import ctypes
+
+    from speculative_decoding_verify_mla_amd import build as tvbuild
+
+    dev = "cuda"
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del src, dst
+    out = {"hbm_copy_GBps": round(copy_gbs, 1)}
+    if not os.path.exists(tvbuild.PROBE_LIB):
+        out["mfma_bf16_TFLOPs"] = None
+        return out
+    probe = ctypes.CDLL(tvbuild.PROBE_LIB)
+    probe.tvmla_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.tvmla_probe_mfma_flops.restype = ctypes.c_double
+    probe.tvmla_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    blocks, iters = 512, 2000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        assert probe.tvmla_probe_mfma_bf16(sink.data_ptr(), blocks, iters, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        probe.tvmla_probe_mfma_bf16(sink.data_ptr(), blocks, iters, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    out["mfma_bf16_TFLOPs"] = round(probe.tvmla_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12, 1)
+    return out
 
 
 def profiled_traffic(kernel):
@@ -219,6 +323,8 @@ def main(argv=None):
                     help="defrag: time tvmla_defrag on the workload (a separate diagnostic line, not the "
                          "verify bench line) and the verify step before and after compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", action="store_true",
+                    help="one diagnostic line per synthetic configuration instead of the bench line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the verify step, time a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM traffic counters)")
@@ -255,14 +361,32 @@ def main(argv=None):
         ms = e0.elapsed_time(e1) / args.steps
         print(json.dumps({"copy_bytes": n, "ms": ms, "read_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return 0
+    if args.report:
+        return report(args, torch, binding)
     w = gen.build(args.workload, **({"nsplit": args.nsplit} if args.nsplit else {}))
     if args.op == "defrag":
         return bench_defrag(args, w, torch, binding)
     if args.op == "tree_mask":
         return bench_tree_mask(args, w, torch, binding)
+    res = measure(args, w, args.workload, torch, binding)
+    res["measured_peaks"] = measured_peaks(torch)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        host_pool = w.host_pool(fill=0.0)
+        res["cpu_baseline"] = cpu_baseline(w, host_pool)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def measure(args, w, name, torch, binding, graph=True):
+    """The verify call on workload w: eager step, split-only and combine-only
+    times, the roofline of the split kernel, and (graph=True) the call
+    replayed from a HIP graph, warm and cold. Returns the bench line."""
+    dev = "cuda"
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
-    # the split count the full call runs (raised above ns only when the grid would leave CUs idle);
-    # the split-only and combine-only timings use it too, so they time the same launches as the step
+    # the split count the full call runs (tvmla_effective_nsplit); the
+    # split-only and combine-only timings use it too, so they time the same
+    # launches as the step
     ns_eff = binding.effective_nsplit(w.batch, T, H, ns)
     algo_used = args.algo or binding.auto_algo(w.batch, T, H, ns, 0 if w.spec.dtype == "bf16" else 1)
     kernel = KERNEL_OF_ALGO.get(algo_used, "split")
@@ -277,9 +401,12 @@ def main(argv=None):
     ws = torch.empty(binding.workspace_bytes(w.batch, T, H, ns), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step_on(st):
         binding.verify(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out, lse,
-                       ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
+                       ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=st)
+
+    def step():
+        step_on(stream)
 
     def split_only():
         binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale,
@@ -311,13 +438,14 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] {args.workload}: warmup done", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: warmup done", file=sys.stderr, flush=True)
     ms_step = timed(step, args.steps)
     ms_split = timed(split_only, args.steps)
     ms_combine = timed(combine_only, args.steps)
     assert torch.isfinite(lse).all(), "non-finite lse"
-    print(f"[bench] step {ms_step * 1e3:.1f} us, split {ms_split * 1e3:.1f} us, combine {ms_combine * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {name}: step {ms_step * 1e3:.1f} us, split {ms_split * 1e3:.1f} us, combine "
+          f"{ms_combine * 1e3:.1f} us", file=sys.stderr, flush=True)
+    graph_us = graph_timing(torch, step_on) if graph else None
 
     alg = algorithmic(w)
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
@@ -349,7 +477,7 @@ def main(argv=None):
         "dtype": w.spec.dtype,
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": name,
             "batch": w.batch,
             "prefix": int(w.prefix_lens[0]) if len(set(w.prefix_lens.tolist())) == 1 else "ragged",
             "num_draft": T,
@@ -365,14 +493,43 @@ def main(argv=None):
         },
         "kernels_us": {"split": round(ms_split * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
         "roofline": dict(roof, kernel=kernel,
-                         traffic=profiled_traffic(kernel) if args.workload == "long185k" and args.min_chunk == 0
-                         else None),
+                         traffic=profiled_traffic(kernel) if name == "long185k" and args.min_chunk == 0 else None),
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
-        host_pool = w.host_pool(fill=0.0)
-        res["cpu_baseline"] = cpu_baseline(w, host_pool)
-    print(json.dumps(res), flush=True)
+    if graph_us is not None:
+        res["graph_us"] = graph_us
+    del pool, kv, ws
+    return res
+
+
+def report(args, torch, binding):
+    """One diagnostic line per synthetic configuration (not the bench line):
+    the whole call against both roofs, t_HBM = all algorithmic bytes / 8 TB/s
+    and t_compute = flops / the dtype's peak (bf16 MFMA 2.5 PFLOP/s; fp32
+    vector 157.3 TFLOP/s for the fp32 configuration)."""
+    from workloads import gen
+
+    for name in REPORT_WORKLOADS:
+        w = gen.build(name)
+        r = measure(args, w, name, torch, binding)
+        alg = algorithmic(w)
+        t = r["us_per_call"] * 1e-6
+        peak = MFMA_BF16_PEAK_TFLOPS if w.spec.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+        t_hbm = alg["all_bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_cmp = alg["flops"] / (peak * 1e12)
+        line = {
+            "metric": "verify call per configuration: us, KV-read GB/s, roofline fractions",
+            "workload": name, "dtype": w.spec.dtype, "us_per_call": r["us_per_call"], "graph_us": r["graph_us"],
+            "kv_GBps": r["value"], "hbm_frac": r["hbm_frac"],
+            "compute_frac": round(t_cmp / t, 4), "compute_peak_TFLOPs": peak,
+            "bound": "hbm" if t_hbm >= t_cmp else ("mfma" if w.spec.dtype == "bf16" else "valu"),
+            "roofline_frac": round(max(t_hbm, t_cmp) / t, 4),
+            "t_hbm_us": round(t_hbm * 1e6, 2), "t_compute_us": round(t_cmp * 1e6, 2),
+            "kernels_us": r["kernels_us"], "split_roofline": r["roofline"],
+            "config": r["config"],
+        }
+        print(json.dumps(line), flush=True)
+        del w
+        torch.cuda.empty_cache()
     return 0
 
 
