@@ -316,10 +316,12 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
  * ceil(num_draft * num_heads / 128) workgroups of the 128-row kernel:
  * nsplit doubled (up to TVMLA_MAX_NSPLIT) while G < 256, i.e. while the
  * requested grid would leave compute units idle (few rows per request, e.g.
- * 8 heads per GPU); else nsplit / 2 when nsplit is even, 256 < G <= 512 and
- * G / 2 >= 256 (one round of longer splits instead of two rounds, each
- * workgroup paying its fixed cost before and after the key loop once);
- * else nsplit. A fixed function of the sizes, so a captured graph keeps its
+ * 8 heads per GPU); else, for 256 < G <= 512, nsplit / 2 when nsplit is
+ * even and G / 2 >= 256 (one round of longer splits instead of two rounds,
+ * each workgroup paying its fixed cost before and after the key loop once);
+ * else nsplit halved while it is even and the halved grid still has >= 1024
+ * workgroups (at least four rounds; fewer partial rows to write and
+ * combine). A fixed function of the sizes, so a captured graph keeps its
  * grid; the workspace size from tvmla_workspace_bytes accounts for it.
  * tvmla_verify_partials and tvmla_combine use nsplit exactly as given.
  * Negative tvmla_status for out-of-range sizes. Host only.

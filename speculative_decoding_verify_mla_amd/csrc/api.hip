@@ -45,23 +45,29 @@ float fold_log2() {
 // Splits the split+combine entry points use: the caller's nsplit doubled
 // (up to TVMLA_MAX_NSPLIT) while the 128-row grid, batch * nsplit * ceil(T*H
 // / 128) workgroups, would not cover the 256 compute units -- the shapes with
-// few rows per request (8 heads per GPU) -- and halved once when that grid
-// needs more than one but at most two rounds. A function of the sizes only, so
+// few rows per request (8 heads per GPU) -- else halved as described below.
+// A function of the sizes only, so
 // the grid stays fixed for graph capture; results equal those at nsplit up
 // to rounding (the LSE merge is exact in real arithmetic).
 int32_t effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
   if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return nsplit;
   const int64_t groups = ((int64_t)num_draft * num_heads + 127) / 128;
   int32_t ns = nsplit;
-  while ((int64_t)batch * ns * groups < 256 && 2 * ns <= TVMLA_MAX_NSPLIT) ns *= 2;
-  // A grid of more than one but at most two rounds of 256 workgroups runs as
-  // one round of splits twice as long: each workgroup's fixed cost (queries,
-  // split bounds and first tile before the loop, the partial-row writes
-  // after it) is paid once instead of twice, and the combine reads half the
-  // partial rows.
-  if (ns == nsplit && ns % 2 == 0 && (int64_t)batch * ns * groups > 256 && (int64_t)batch * ns * groups <= 512 &&
-      (int64_t)batch * (ns / 2) * groups >= 256)
-    ns /= 2;
+  auto grid = [&](int32_t n) { return (int64_t)batch * n * groups; };
+  while (grid(ns) < 256 && 2 * ns <= TVMLA_MAX_NSPLIT) ns *= 2;
+  if (ns != nsplit) return ns;
+  // Fewer, longer splits where the grid has workgroups to spare. Each
+  // workgroup pays a fixed cost (queries, split bounds and first tile
+  // before the key loop, the partial-row writes after it) and every split
+  // adds a partial row per query row for the combine to read. A grid of more
+  // than one but at most two rounds of 256 workgroups runs as one round;
+  // a larger one is halved while at least four rounds remain, which still
+  // balances ragged batches over the compute units.
+  if (grid(ns) > 256 && grid(ns) <= 512) {
+    if (ns % 2 == 0 && grid(ns / 2) >= 256) ns /= 2;
+  } else {
+    while (ns % 2 == 0 && grid(ns / 2) >= 1024) ns /= 2;
+  }
   return ns;
 }
 

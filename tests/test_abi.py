@@ -66,7 +66,11 @@ def test_effective_nsplit(lib):
     assert ens(1, 16, 64, 63) == 63          # 504 workgroups, odd count: kept
     assert ens(1, 16, 64, 48) == 48          # 384 workgroups: halving would leave CUs idle
     assert ens(1, 16, 64, 32) == 32          # exactly one round
-    assert ens(2, 16, 64, 64) == 64          # 1024 workgroups: many rounds, kept
+    assert ens(2, 16, 64, 64) == 64          # 1024 workgroups: halving would leave fewer than four rounds
+    assert ens(2, 16, 64, 128) == 64         # 2048 workgroups: halved once
+    assert ens(32, 8, 64, 64) == 8           # 32 requests x 4 row groups: 8192 workgroups, halved down to 1024
+    assert ens(8, 32, 64, 64) == 8           # 8 requests x 16 row groups: likewise
+    assert ens(8, 32, 64, 63) == 63          # odd: kept
     assert ens(1, 16, 8, 64) == 256          # one row group: doubled twice
     assert ens(3, 5, 8, 7) == 112            # 3 x 56 = 168 < 256, 3 x 112 = 336
     assert ens(1, 1, 1, 64) == 256

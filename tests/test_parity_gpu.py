@@ -359,11 +359,13 @@ def test_graph_capture_replay():
 @pytest.mark.parametrize("name,ns,eff_expected", [
     ("ragged_h8", 7, 112),   # 3 requests x 40 rows: 21 workgroups, raised to 336
     ("groups_h64", 32, 16),  # 2 requests x 8 row groups: 512 workgroups, lowered to one round of 256
+    ("groups4_h64", 64, 32),  # 4 requests x 8 row groups: 2048 workgroups, halved to 1024 (four rounds)
 ])
 def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
     """The full call runs the effective split count; it is bit-identical to
     split + combine at that count, and matches the oracle."""
-    w = gen.build(SMALL[name])
+    spec = SMALL[name] if name in SMALL else gen.small(name, 4, [40, 300, 0, 129], 16, 64, seed=19)
+    w = gen.build(spec)
     eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, ns)
     assert eff == eff_expected
     ref_out, ref_lse = _oracle(w)
