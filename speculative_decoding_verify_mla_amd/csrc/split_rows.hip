@@ -236,7 +236,9 @@ __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra
   const int k = 16 * wave + u;
   const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
-  const char* src = reinterpret_cast<const char*>(row_addr) + ((lane ^ piece_swz(k)) << 4);
+  // (an unsigned 32-bit offset: the load takes the uniform row address as its
+  // scalar base and one offset register, with no 64-bit address arithmetic)
+  const char* src = reinterpret_cast<const char*>(row_addr) + (uint32_t)((lane ^ piece_swz(k)) << 4);
   __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 0);
 }
 
