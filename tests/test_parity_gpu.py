@@ -86,6 +86,20 @@ def test_small_cases_full(name):
         compare(w, out, lse, ref_out, ref_lse, f"{name}/algo{algo}")
 
 
+@pytest.mark.parametrize("batch,prefix,T,H", [
+    (1, [300], 16, 64),             # 1024 rows: the combine runs 4 wavefronts per row
+    (4, [50, 0, 130, 7], 16, 64),   # 4096 rows: one wavefront per row, four rows per workgroup
+])
+def test_fp32_combine_widths(batch, prefix, T, H):
+    """fp32 queries (scalar split kernel, fp32 partial rows) at row counts that
+    take the combine's 4- and 1-wavefront-per-row forms."""
+    w = gen.build(gen.small("fp32_wide", batch, prefix, T, H, dtype="fp32", seed=23))
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w)
+    out, lse = d.result(algo=SCALAR)
+    compare(w, out, lse, ref_out, ref_lse, f"fp32_wide/{batch}x{T}x{H}")
+
+
 @pytest.mark.parametrize("nsplit", [1, 3, 64, 200, 256])
 def test_nsplit_invariance(nsplit):
     w = gen.build("p4096")
