@@ -9,7 +9,7 @@ paging scatters a request's cache rows over the pool, so reading them is a
 gather of isolated rows ("The Plan Document: A Pivot Point in Custom CUDA
 Kernel Development", section "Context: The Bottleneck That Demanded a Custom
 Kernel"), and the plan's last phase is KV defragmentation (same page, section
-"Output Knowledge Created"). The reading taken here (listed in the design doc):
+"Output Knowledge Created"). The reading taken here, since they give no interface:
 
   for each request b, prefix position p in [0, P_b), P_b = kv_indptr[b+1] -
   kv_indptr[b]:

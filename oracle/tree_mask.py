@@ -13,7 +13,7 @@ Required", DDTree paragraph), passed raw as custom_mask + mask_indptr
 device removes host marshaling around the verify call (the directive quoted
 in the same page's introduction).
 
-Definition (readings listed in the design doc): request b has P_b prefix keys and
+Definition (a reading of the pages, which give no formula): request b has P_b prefix keys and
 T draft nodes; node 0 is the root (parent -1) and parent[i] < i. Row i of the
 request's [T][P_b + T] byte block is
     1 at every prefix column p < P_b,

@@ -31,7 +31,7 @@ The split-K form (partials per key range, then a log-sum-exp merge; page 1,
 the same result exactly up to rounding; `split_range`, `verify_partials` and
 `combine` write that schedule out so tests can check the identity.
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * kv_indptr spans the prefix only; the T draft tokens follow it, so a
     request has N_b = P_b + T keys in the order prefix, then draft nodes.
   * The mask row for draft token i of request b starts at
