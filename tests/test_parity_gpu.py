@@ -100,6 +100,21 @@ def test_fp32_combine_widths(batch, prefix, T, H):
     compare(w, out, lse, ref_out, ref_lse, f"fp32_wide/{batch}x{T}x{H}")
 
 
+@pytest.mark.parametrize("algo", [ROWS, MFMA, SCALAR])
+def test_packed_query_views(algo):
+    """A packed [tokens, heads, 576] query passed as two strided views (latent
+    part and rope part of each row) gives the same bits as two contiguous
+    tensors."""
+    w = gen.build(SMALL["groups_h64"])
+    d = Device(w)
+    o1, l1 = d.result(algo=algo)
+    packed = torch.cat([d.q_nope, d.q_rope], dim=-1).contiguous()  # [tokens, heads, 576]
+    d.q_nope, d.q_rope = packed[..., :512], packed[..., 512:]
+    assert d.q_nope.stride() == (w.num_heads * 576, 576, 1)
+    o2, l2 = d.result(algo=algo)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 @pytest.mark.parametrize("nsplit", [1, 3, 64, 200, 256])
 def test_nsplit_invariance(nsplit):
     w = gen.build("p4096")
