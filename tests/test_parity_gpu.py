@@ -55,6 +55,8 @@ SMALL = {
     "t64_h2": gen.small("t64_h2", 1, [100], 64, 2, seed=14),
     # largest head count
     "t2_h128": gen.small("t2_h128", 1, [50], 2, 128, seed=15),
+    # largest tree at the largest head count: 8192 rows, 64 row groups of 128
+    "t64_h128": gen.small("t64_h128", 1, [100], 64, 128, seed=18),
     # chain tree over a longer prefix
     "chain_h16": gen.small("chain_h16", 2, [700, 65], 8, 16, tree="chain", seed=16),
     # fp32 through the scalar kernel, ragged
