@@ -267,8 +267,8 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const int g = kq - jq * groups;
   const int pair = xcd + 8 * jq;
   if (pair >= pairs) return;
-  const int b = pair / p.nsplit;
-  const int s = pair - b * p.nsplit;
+  const int b = request_of_rank(p, pair / p.nsplit);
+  const int s = pair - (pair / p.nsplit) * p.nsplit;
 
   const int Rw = p.num_draft * p.num_heads;  // partial-row stride of the workspace
   int Tb;

@@ -113,6 +113,35 @@ __device__ inline void request_tokens(const int64_t* qo_indptr, int num_draft, i
   Tb = n < 0 ? 0 : (n > num_draft ? num_draft : (int)n);
 }
 
+// Request served by the (request, split) pairs of rank `rank`, longest
+// request first. Workgroups start roughly in id order and pair indices grow
+// with the id, so handing the first pairs to the requests with the most keys
+// (all splits of a request are equally long) lets the short requests fill
+// the compute units at the end: longest-processing-time-first list
+// scheduling, where index order can leave a few long workgroups running
+// alone. The order is a function of the device-side lengths, so the grid
+// stays fixed. Rank of request j = number of requests with more keys, or as
+// many keys and a lower index (a strict total order, so the ranks are a
+// permutation and exactly one lane matches). Every lane of the wavefront
+// must be active. Batches of one or of more than 64 keep index order.
+__device__ inline int request_of_rank(const SplitParams& p, int rank) {
+  if (p.batch <= 1 || p.batch > 64) return rank;
+  const int lane = threadIdx.x & 63;
+  int n = -1;
+  if (lane < p.batch) {
+    int Tb;
+    int64_t t0;
+    request_tokens(p.qo_indptr, p.num_draft, lane, Tb, t0);
+    n = p.kv_indptr[lane + 1] - p.kv_indptr[lane] + Tb;
+  }
+  int above = 0;
+  for (int j = 0; j < p.batch; ++j) {
+    const int nj = __builtin_amdgcn_readlane(n, j);
+    above += (nj > n || (nj == n && j < lane)) ? 1 : 0;
+  }
+  return __builtin_ctzll(__ballot(lane < p.batch && above == rank));
+}
+
 // Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -63,6 +63,10 @@ SMALL = {
     "fp32_ragged": gen.small("fp32_ragged", 3, [0, 9, 130], 4, 8, dtype="fp32", seed=17),
     # many short requests: 19,200 (request, split) pairs, 7,200 output rows (one combine wavefront each)
     "many_requests": gen.small("many_requests", 300, (0, 64), 3, 8, pool_slots=1 << 15, seed=18),
+    # 64 requests of random lengths (the largest batch the split kernels order longest first)
+    "b64_ragged": gen.small("b64_ragged", 64, (0, 400), 2, 8, pool_slots=1 << 15, seed=19),
+    # equal lengths in one batch: the longest-first order breaks ties by request index
+    "ties": gen.small("ties", 5, [60, 300, 60, 300, 60], 3, 16, seed=20),
 }
 
 
