@@ -319,9 +319,10 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
  * 8 heads per GPU); else, for 256 < G <= 512, nsplit / 2 when nsplit is
  * even and G / 2 >= 256 (one round of longer splits instead of two rounds,
  * each workgroup paying its fixed cost before and after the key loop once);
- * else nsplit halved while it is even and the halved grid still has >= 1024
- * workgroups (at least four rounds; fewer partial rows to write and
- * combine). A fixed function of the sizes, so a captured graph keeps its
+ * else nsplit halved while it is even and the halved grid still has >= 512
+ * workgroups when batch <= 64 (at least two rounds: such batches are served
+ * longest request first) or >= 1024 for larger batches (four rounds); fewer
+ * partial rows to write and combine. A fixed function of the sizes, so a captured graph keeps its
  * grid; the workspace size from tvmla_workspace_bytes accounts for it.
  * tvmla_verify_partials and tvmla_combine use nsplit exactly as given.
  * Negative tvmla_status for out-of-range sizes. Host only.

@@ -61,12 +61,15 @@ int32_t effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, in
   // before the key loop, the partial-row writes after it) and every split
   // adds a partial row per query row for the combine to read. A grid of more
   // than one but at most two rounds of 256 workgroups runs as one round;
-  // a larger one is halved while at least four rounds remain, which still
-  // balances ragged batches over the compute units.
+  // a larger one is halved while at least two rounds remain (batches of up
+  // to 64 requests, which the split kernels serve longest request first) or
+  // four (larger batches, served in index order), which still balances
+  // ragged lengths over the compute units.
   if (grid(ns) > 256 && grid(ns) <= 512) {
     if (ns % 2 == 0 && grid(ns / 2) >= 256) ns /= 2;
   } else {
-    while (ns % 2 == 0 && grid(ns / 2) >= 1024) ns /= 2;
+    const int64_t keep = batch <= 64 ? 512 : 1024;
+    while (ns % 2 == 0 && grid(ns / 2) >= keep) ns /= 2;
   }
   return ns;
 }

@@ -66,10 +66,13 @@ def test_effective_nsplit(lib):
     assert ens(1, 16, 64, 63) == 63          # 504 workgroups, odd count: kept
     assert ens(1, 16, 64, 48) == 48          # 384 workgroups: halving would leave CUs idle
     assert ens(1, 16, 64, 32) == 32          # exactly one round
-    assert ens(2, 16, 64, 64) == 64          # 1024 workgroups: halving would leave fewer than four rounds
-    assert ens(2, 16, 64, 128) == 64         # 2048 workgroups: halved once
-    assert ens(32, 8, 64, 64) == 8           # 32 requests x 4 row groups: 8192 workgroups, halved down to 1024
-    assert ens(8, 32, 64, 64) == 8           # 8 requests x 16 row groups: likewise
+    assert ens(2, 16, 64, 64) == 32          # 1024 workgroups: halved to two rounds
+    assert ens(2, 16, 64, 128) == 32         # 2048 workgroups: halved twice
+    assert ens(32, 8, 64, 64) == 4           # 32 requests x 4 row groups: 8192 workgroups, halved down to 512
+    assert ens(8, 32, 64, 64) == 4           # 8 requests x 16 row groups: likewise
+    assert ens(96, 8, 64, 64) == 4           # 96 requests (index order): halved while four rounds remain
+    assert ens(64, 8, 64, 64) == 2           # 64 requests (longest first): two rounds
+    assert ens(3, 16, 64, 32) == 32          # 768 workgroups: halving would leave fewer than two rounds
     assert ens(8, 32, 64, 63) == 63          # odd: kept
     assert ens(1, 16, 8, 64) == 256          # one row group: doubled twice
     assert ens(3, 5, 8, 7) == 112            # 3 x 56 = 168 < 256, 3 x 112 = 336
@@ -164,7 +167,7 @@ def test_small_workspace(lib):
 
 def test_combine_errors(lib):
     f = lib.tvmla_combine
-    # 2 requests x 16 tokens x 64 heads x 64 splits: 1024 workgroups, so the workspace is sized for exactly 64 splits
+    # 2 requests x 16 tokens x 64 heads x 64 splits: the call runs 32, so the workspace is sized for exactly 64 splits
     ws = binding.workspace_bytes(2, 16, 64, 64)
     assert f(_FAKE, ws, _FAKE, 2, 16, 64, 64, 0, 5, _FAKE, _FAKE, None) == 3
     assert f(_FAKE, ws, _FAKE, 2, 16, 64, 64, 0, 0, None, _FAKE, None) == 1
