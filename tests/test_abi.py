@@ -160,6 +160,36 @@ def test_misaligned(lib, kw):
     assert _call(lib, **kw) == 5
 
 
+def test_effective_nsplit_sweep(lib):
+    """The library's split count against the rule as its header states it,
+    over a grid of sizes (host-only call, no GPU needed)."""
+
+    def stated(batch, T, H, ns):
+        groups = -(-(T * H) // 128)
+        grid = lambda n: batch * n * groups
+        e = ns
+        while grid(e) < 256 and 2 * e <= 256:
+            e *= 2
+        if e != ns:
+            return e
+        if 256 < grid(e) <= 512:
+            return e // 2 if e % 2 == 0 and grid(e // 2) >= 256 else e
+        keep = 512 if batch <= 64 else 1024
+        while e % 2 == 0 and grid(e // 2) >= keep:
+            e //= 2
+        return e
+
+    n = 0
+    for batch in (1, 2, 3, 7, 32, 64, 65, 300):
+        for T, H in ((1, 1), (4, 8), (5, 8), (16, 8), (16, 64), (8, 64), (32, 64), (64, 128)):
+            for ns in (1, 3, 7, 8, 32, 48, 63, 64, 128, 200, 256):
+                got = binding.effective_nsplit(batch, T, H, ns)
+                assert got == stated(batch, T, H, ns), (batch, T, H, ns, got)
+                assert 1 <= got <= 256
+                n += 1
+    assert n == 8 * 8 * 11
+
+
 def test_small_workspace(lib):
     need = binding.workspace_bytes(1, 4, 64, 64)
     assert _call(lib, ws_bytes=need - 1) == 4
