@@ -67,12 +67,6 @@ def _i64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.int64)
 
 
-def prefix_length(kv_indptr, b: int) -> int:
-    """P_b = kv_indptr[b+1] - kv_indptr[b] (page 1, "The Design Emerges", fourth insight)."""
-    ip = _i64(kv_indptr)
-    return int(ip[b + 1] - ip[b])
-
-
 def key_slots(kv_indptr, kv_indices, out_cache_loc, b: int, num_draft: int) -> np.ndarray:
     """Pool slot of each of request b's N_b keys: prefix via kv_indices, then
     drafts via out_cache_loc (page 1, "The Design Emerges", second insight)."""

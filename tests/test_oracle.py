@@ -385,3 +385,104 @@ def _split_drops_last(n, ns, s):
 def test_planted_mistakes_are_caught(monkeypatch, attr, fn):
     fails = _pins_fail(monkeypatch, attr, fn)
     assert fails, f"planted mistake in {attr} ({fn.__name__}) passed every pin"
+
+
+# ---------------------------------------------------------------- row picks and request slices
+#
+# verify_rows (the oracle of chosen (token, head) rows) has its own indexing:
+# it groups the picks by request (t // T), takes token t's query and the mask
+# row t - b*T. It is pinned against the brute-force oracle directly, over
+# several requests (b > 0), the first and last token and head, picks in
+# scrambled order with repeats; planted indexing mistakes must fail that pin.
+
+
+def _row_picks(w):
+    T, H = w.num_draft, w.num_heads
+    picks = []
+    for b in range(w.batch):
+        picks += [(b * T, 0), (b * T + T - 1, H - 1), (b * T + T // 2, H // 2), (b * T, H - 1)]
+    rng = np.random.default_rng(0)
+    picks += [picks[i] for i in rng.permutation(len(picks))[:3]]  # repeats
+    return [picks[i] for i in rng.permutation(len(picks))]
+
+
+def _check_rows_against_brute(rows_fn):
+    w = _tiny(seed=51, batch=3, prefix=(6, 0, 11), T=4, H=3, dtype="bf16")
+    args = _args(w)
+    picks = _row_picks(w)
+    out, lse = rows_fn(*args, picks)
+    bo, bl = brute.verify_brute(*args)
+    for k, (t, h) in enumerate(picks):
+        np.testing.assert_allclose(out[k], np.array(bo[t][h]), rtol=1e-12, atol=1e-12)
+        assert lse[k] == pytest.approx(bl[t][h], rel=1e-12, abs=1e-12)
+
+
+def test_verify_rows_matches_brute():
+    _check_rows_against_brute(vo.verify_rows)
+
+
+def test_verify_rows_matches_verify_medium():
+    """A medium bf16 case (ragged prefixes, 16 heads): every pick equals the
+    whole-batch oracle's row."""
+    w = gen.build(gen.small("rows", 3, [300, 17, 1000], 8, 16, pool_slots=4096, seed=52))
+    args = _args(w)
+    out, lse = vo.verify(*args)
+    picks = _row_picks(w)
+    ro, rl = vo.verify_rows(*args, picks)
+    for k, (t, h) in enumerate(picks):
+        np.testing.assert_allclose(ro[k], out[t, h], rtol=1e-12, atol=1e-12)
+        assert rl[k] == pytest.approx(lse[t, h], rel=1e-12, abs=1e-12)
+
+
+def _rows_variant(mistake):
+    """verify_rows with one plausible indexing mistake planted."""
+
+    def rows(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr, sm_scale,
+             num_draft, picks):
+        T = num_draft
+        out = np.zeros((len(picks), vo.D_LATENT))
+        lse = np.zeros(len(picks))
+        for k, (t, h) in enumerate(picks):
+            b = t // T
+            kb = (b + 1) % (len(vo._i64(kv_indptr)) - 1) if mistake == "keys_of_next_request" else b
+            slots = vo.key_slots(kv_indptr, kv_indices, out_cache_loc, kb, T)
+            keys = vo.request_keys(kv_cache, slots)
+            vis = vo.visibility(custom_mask, mask_indptr, kb, T, len(slots))
+            i = {"mask_row_first": 0, "mask_row_global": t % vis.shape[0] if b == 0 else (t + 1) % T}.get(
+                mistake, t - b * T)
+            hq = 0 if mistake == "head_zero" else h
+            qn = vo._f64(q_nope[t, hq])[None]
+            qr = vo._f64(q_rope[t, hq])[None]
+            o, ls = vo.attend(qn, qr, keys, vis[i][None], sm_scale)
+            out[k], lse[k] = o[0], ls[0]
+        return out, lse
+
+    return rows
+
+
+def test_rows_variant_without_mistake_passes():
+    _check_rows_against_brute(_rows_variant("none"))
+
+
+@pytest.mark.parametrize("mistake", ["keys_of_next_request", "mask_row_first", "mask_row_global", "head_zero"])
+def test_rows_planted_mistakes_are_caught(mistake):
+    with pytest.raises(AssertionError):
+        _check_rows_against_brute(_rows_variant(mistake))
+
+
+def test_request_slice_equals_whole_batch():
+    """The oracle run on one request's slice of the batch arrays (its query
+    rows and draft slots, kv_indptr[b:b+2] and mask_indptr[b:b+2] keeping
+    their absolute offsets) equals that request's rows of the whole-batch
+    oracle: the GPU tests check whole requests of the largest workload this
+    way."""
+    w = _tiny(seed=53, batch=3, prefix=(40, 0, 75), T=5, H=4, dtype="bf16")
+    pool = w.host_pool()
+    out, lse = vo.verify(*_args(w, pool))
+    T = w.num_draft
+    for b in range(w.batch):
+        rows = slice(b * T, (b + 1) * T)
+        o, l = vo.verify(w.q_nope[rows], w.q_rope[rows], pool, w.kv_indptr[b:b + 2], w.kv_indices,
+                         w.out_cache_loc[rows], w.custom_mask, w.mask_indptr[b:b + 2], w.sm_scale, T)
+        np.testing.assert_array_equal(o, out[rows])
+        np.testing.assert_array_equal(l, lse[rows])
