@@ -2,13 +2,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long185k]
 
-One step = one tvmla_verify call (split kernel + combine kernel) over the
-whole synthetic batch, inputs resident in HBM. Prints ONE JSON line:
-value = effective KV-read GB/s (cache-row bytes the call must read / time per
-call), plus us per call, the split kernel's MFMA roofline fraction (timed
-live with HIP events through tvmla_verify_partials on the same stream), and
-the fp64 CPU oracle timed on a bounded sample of the same workload. The line
-also carries the call captured in a HIP graph and replayed warm and cold
+One step = one verify call (split kernel + combine kernel) over the whole
+synthetic batch, inputs resident in HBM: tvmla_verify_ex with
+TVMLA_FLAG_TUNE_NSPLIT (the workload's NSPLIT adapted to the 256 compute
+units). Prints ONE JSON line: value = effective KV-read GB/s (cache-row bytes
+the call must read / time per call), plus us per call, the split kernel's
+MFMA roofline fraction (timed live with HIP events through
+tvmla_verify_partials on the same stream), and the fp64 CPU oracle timed on
+the same workload (whole, or a bounded sample). The line also carries the
+pages' own call -- tvmla_verify at exactly the workload's NSPLIT -- timed
+the same way, the call captured in a HIP graph and replayed warm and cold
 (L2 and MALL flushed before each replay), and the HBM copy bandwidth and
 bf16 MFMA rate measured on the same GPU.
 
@@ -101,12 +104,26 @@ def graph_timing(torch, call_on, replays=GRAPH_REPLAYS):
     return res
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libtvmla_probe.so")
+
+
+def build_probe(verbose=False):
+    """Compile the matrix-core throughput probe (bench infrastructure, not
+    part of libtvmla.so) into libtvmla_probe.so beside this file:
+    python bench.py --build-probe (on the build machine, before a GPU run)."""
+    from speculative_decoding_verify_mla_amd import build as tvbuild
+
+    tmp = PROBE_LIB + ".tmp"
+    tvbuild._run([tvbuild.HIPCC, *tvbuild.CFLAGS, "-shared", "-o", tmp, PROBE_SRC], verbose)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def measured_peaks(torch):
     """HBM bandwidth of a plain 1 GiB device copy (read + write bytes) and
     the bf16 MFMA rate of the throughput probe, on this GPU."""
     import ctypes
-
-    from speculative_decoding_verify_mla_amd import build as tvbuild
 
     dev = "cuda"
     n = 1 << 30
@@ -124,10 +141,10 @@ def measured_peaks(torch):
     copy_gbs = 2 * n / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
     del src, dst
     out = {"hbm_copy_GBps": round(copy_gbs, 1)}
-    if not os.path.exists(tvbuild.PROBE_LIB):
+    if not os.path.exists(PROBE_LIB):
         out["mfma_bf16_TFLOPs"] = None
         return out
-    probe = ctypes.CDLL(tvbuild.PROBE_LIB)
+    probe = ctypes.CDLL(PROBE_LIB)
     probe.tvmla_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     probe.tvmla_probe_mfma_flops.restype = ctypes.c_double
     probe.tvmla_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -173,12 +190,7 @@ def cpu_baseline(w, pool_host):
     otherwise the rows of the first draft tokens (all heads), scaled."""
     from oracle import verify_fp64 as vo
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the OMP setting
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = blas_threads()
     T, H = w.num_draft, w.num_heads
     rows = w.batch * T * H
     kv = algorithmic(w)["kv_bytes"]
@@ -202,7 +214,33 @@ def cpu_baseline(w, pool_host):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{what} in {dt:.2f} s; value = cache-row bytes x {frac:.4f} / time",
+        "seconds": round(dt, 3),
+        "cpu_model": cpu_model(),
+        "cpu_count": os.cpu_count(),
     }
+
+
+def blas_threads():
+    """Threads the fp64 oracle's BLAS runs with (its matrix products are
+    where the oracle spends its time)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the OMP setting
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_defrag(args, w, torch, binding):
@@ -323,6 +361,8 @@ def main(argv=None):
                     help="defrag: time tvmla_defrag on the workload (a separate diagnostic line, not the "
                          "verify bench line) and the verify step before and after compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--build-probe", action="store_true",
+                    help="compile the MFMA throughput probe (libtvmla_probe.so) and exit; no GPU needed")
     ap.add_argument("--report", action="store_true",
                     help="one diagnostic line per synthetic configuration instead of the bench line")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -330,6 +370,9 @@ def main(argv=None):
                          "(reference kernel for scaling HBM traffic counters)")
     args = ap.parse_args(argv)
 
+    if args.build_probe:
+        print(build_probe(verbose=True))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verify path shards by heads or requests with no exchange)", file=sys.stderr)
@@ -371,7 +414,7 @@ def main(argv=None):
     res = measure(args, w, args.workload, torch, binding)
     res["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         host_pool = w.host_pool(fill=0.0)
         res["cpu_baseline"] = cpu_baseline(w, host_pool)
     print(json.dumps(res), flush=True)
@@ -384,11 +427,13 @@ def measure(args, w, name, torch, binding, graph=True):
     replayed from a HIP graph, warm and cold. Returns the bench line."""
     dev = "cuda"
     T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
-    # the split count the full call runs (tvmla_effective_nsplit); the
+    dcode = 0 if w.spec.dtype == "bf16" else 1
+    # the split count the tuned call runs (tvmla_effective_nsplit); the
     # split-only and combine-only timings use it too, so they time the same
     # launches as the step
     ns_eff = binding.effective_nsplit(w.batch, T, H, ns)
-    algo_used = args.algo or binding.auto_algo(w.batch, T, H, ns, 0 if w.spec.dtype == "bf16" else 1)
+    algo_used = args.algo or binding.auto_algo(w.batch, T, H, ns_eff, dcode)
+    algo_exact = args.algo or binding.auto_algo(w.batch, T, H, ns, dcode)
     kernel = KERNEL_OF_ALGO.get(algo_used, "split")
     pool = w.device_pool(dev, fill=0.0)
     kv = pool
@@ -403,10 +448,19 @@ def measure(args, w, name, torch, binding, graph=True):
 
     def step_on(st):
         binding.verify(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out, lse,
-                       ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=st)
+                       ws, T, algo=args.algo, min_chunk=args.min_chunk, flags=binding.TUNE_NSPLIT, stream=st)
 
     def step():
         step_on(stream)
+
+    def exact_step():
+        # the pages' call: exactly the workload's NSPLIT
+        if args.algo == 0 and args.min_chunk == 0:
+            binding.verify_plain(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns,
+                                 out, lse, ws, T, stream=stream)
+        else:
+            binding.verify(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out,
+                           lse, ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
 
     def split_only():
         binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale,
@@ -443,8 +497,13 @@ def measure(args, w, name, torch, binding, graph=True):
     ms_split = timed(split_only, args.steps)
     ms_combine = timed(combine_only, args.steps)
     assert torch.isfinite(lse).all(), "non-finite lse"
+    for _ in range(args.warmup):
+        exact_step()
+    ms_exact = timed(exact_step, args.steps)
+    assert torch.isfinite(lse).all(), "non-finite lse"
     print(f"[bench] {name}: step {ms_step * 1e3:.1f} us, split {ms_split * 1e3:.1f} us, combine "
-          f"{ms_combine * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"{ms_combine * 1e3:.1f} us; tvmla_verify at nsplit {ns}: {ms_exact * 1e3:.1f} us", file=sys.stderr,
+          flush=True)
     graph_us = graph_timing(torch, step_on) if graph else None
 
     alg = algorithmic(w)
@@ -492,6 +551,9 @@ def measure(args, w, name, torch, binding, graph=True):
             "flops": alg["flops"],
         },
         "kernels_us": {"split": round(ms_split * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
+        "nsplit_exact_call": {"api": "tvmla_verify", "nsplit": ns, "algo": algo_exact,
+                              "us_per_call": round(ms_exact * 1e3, 2),
+                              "kv_GBps": round(alg["kv_bytes"] / (ms_exact * 1e-3) / 1e9, 2)},
         "roofline": dict(roof, kernel=kernel,
                          traffic=profiled_traffic(kernel) if name == "long185k" and args.min_chunk == 0 else None),
     }
@@ -505,7 +567,9 @@ def report(args, torch, binding):
     """One diagnostic line per synthetic configuration (not the bench line):
     the whole call against both roofs, t_HBM = all algorithmic bytes / 8 TB/s
     and t_compute = flops / the dtype's peak (bf16 MFMA 2.5 PFLOP/s; fp32
-    vector 157.3 TFLOP/s for the fp32 configuration)."""
+    vector 157.3 TFLOP/s for the fp32 configuration), and the fp64 oracle
+    timed once per configuration on the host cores (thread count and CPU
+    model recorded)."""
     from workloads import gen
 
     for name in REPORT_WORKLOADS:
@@ -525,8 +589,12 @@ def report(args, torch, binding):
             "roofline_frac": round(max(t_hbm, t_cmp) / t, 4),
             "t_hbm_us": round(t_hbm * 1e6, 2), "t_compute_us": round(t_cmp * 1e6, 2),
             "kernels_us": r["kernels_us"], "split_roofline": r["roofline"],
+            "nsplit_exact_call": r["nsplit_exact_call"],
             "config": r["config"],
         }
+        if not args.no_cpu_baseline:
+            print(f"[bench] {name}: timing the CPU oracle", file=sys.stderr, flush=True)
+            line["cpu_baseline"] = cpu_baseline(w, w.host_pool(fill=0.0))
         print(json.dumps(line), flush=True)
         del w
         torch.cuda.empty_cache()

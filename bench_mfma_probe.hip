@@ -1,7 +1,8 @@
 // Matrix-core throughput probe for gfx950: the dense bf16 MFMA rate this part
 // sustains, measured beside the split kernel so its MFMA fraction can be read
 // against the hardware as well as against the published peak. Not part of
-// the verify path; bench.py loads it from libtvmla_probe.so.
+// the verify path: bench.py compiles it (build_probe) into
+// libtvmla_probe.so beside itself and loads it from there.
 //
 // Every wavefront runs `iters` rounds of eight independent accumulation
 // chains of v_mfma_f32_32x32x16_bf16 (32x32 outputs, k = 16: 32,768 flops

@@ -28,7 +28,9 @@
  *   - Argument checks run on the host before anything is enqueued. On error
  *     the call returns a status != TVMLA_OK and enqueues nothing. Index
  *     CONTENTS (slots, offsets, mask bytes) are trusted: a slot outside the
- *     cache or an offset outside its array is undefined behaviour.
+ *     cache or an offset outside its array is undefined behaviour. A caller
+ *     that cannot vouch for them runs tvmla_check_metadata on host copies
+ *     first.
  *   - Per request b: P_b = kv_indptr[b+1] - kv_indptr[b] prefix keys, then
  *     the T = num_draft draft keys, N_b = P_b + T keys in that order.
  *     Row (t, h) with t = b*T + i is draft token i of request b, head h.
@@ -63,13 +65,15 @@ typedef enum {
   TVMLA_E_ALIGN = 5,     /* a pointer or stride breaks the alignment rules       */
   TVMLA_E_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch             */
   TVMLA_E_ALGO = 7,      /* unknown algorithm selector                           */
-  TVMLA_E_VALUE = 8      /* sm_scale is not a finite positive number              */
+  TVMLA_E_VALUE = 8,     /* sm_scale not finite and positive, unknown flag bits,
+                            or a NaN fold threshold                            */
+  TVMLA_E_INDEX = 9      /* tvmla_check_metadata: an offset or slot out of range */
 } tvmla_status;
 
 typedef enum {
   TVMLA_ALGO_AUTO = 0,   /* bf16 -> ROWS when batch * nsplit * ceil(num_draft *
-                            num_heads / 128) >= 256 (nsplit as effectively used,
-                            see tvmla_effective_nsplit), else MFMA; fp32 -> SCALAR */
+                            num_heads / 128) >= 256 (nsplit = the split count the
+                            call runs), else MFMA; fp32 -> SCALAR             */
   TVMLA_ALGO_SCALAR = 1, /* one wavefront per (row, split); fp32 FMA; any dtype */
   TVMLA_ALGO_MFMA = 2,   /* bf16 MFMA kernel, 64 query rows per workgroup       */
   TVMLA_ALGO_ROWS = 3    /* bf16 MFMA kernel, 128 query rows per workgroup, each
@@ -77,24 +81,42 @@ typedef enum {
 } tvmla_algo;
 
 /*
- * TVMLA_ALGO_ROWS keeps each row's softmax against a reference max and
- * folds its accumulator into the row's workspace slot when the row's max
- * outgrows that reference by more than 2^16 (log2 units). The environment
- * variable TVMLA_FOLD_LOG2 (a number >= 0, read at every call) overrides the
- * 16; results are the same for any value, only the number of folds changes
- * (tests use it to exercise the fold path). Other algorithms ignore it.
+ * Flags of tvmla_verify_ex and tvmla_verify_ragged.
+ *
+ * TVMLA_FLAG_TUNE_NSPLIT: run tvmla_effective_nsplit(batch, num_draft,
+ *   num_heads, nsplit) splits instead of exactly nsplit -- more splits when
+ *   the grid would leave compute units idle, fewer when it would take more
+ *   than one round of workgroups. Still a fixed function of the sizes, so a
+ *   captured graph keeps its grid; the merged result equals the one at
+ *   nsplit up to rounding (the log-sum-exp merge is exact in real
+ *   arithmetic). Without it the call runs exactly the caller's nsplit, the
+ *   fixed split count of "The Architecture of Capture Safety", section "The
+ *   NSPLIT Calculation".
+ */
+#define TVMLA_FLAG_TUNE_NSPLIT 1u
+
+/*
+ * fold_log2 (tvmla_verify_ex, _ragged, _partials): TVMLA_ALGO_ROWS keeps
+ * each row's softmax against a reference max and folds its accumulator into
+ * the row's workspace slot when the row's max outgrows that reference by
+ * more than 2^fold_log2. A negative value selects the default, 16 (every
+ * probability stays below 2^16); NaN is rejected with TVMLA_E_VALUE.
+ * Results are the same for any threshold up to rounding: only the number of
+ * folds changes (small thresholds make folds frequent, which tests use to
+ * exercise that path). Other algorithms ignore it.
  */
 
 /*
- * Bytes of workspace tvmla_verify needs: the per-split partial results
+ * Bytes of workspace a verify call needs: the per-split partial results
  * (page 1, "Assumptions and Their Validity", assumption 3: a fixed
  * workspace sized from batch and constants only). It depends only on its
  * arguments, never on sequence lengths. Returns 0 for out-of-range
  * arguments.
  *
- * The size covers both nsplit splits (the count tvmla_verify_partials and
- * tvmla_combine take as given) and tvmla_effective_nsplit(batch, num_draft,
- * num_heads, nsplit) splits (the count the split+combine entry points use).
+ * The size covers both nsplit splits (the count tvmla_verify runs, and
+ * tvmla_verify_partials and tvmla_combine take as given) and
+ * tvmla_effective_nsplit(batch, num_draft, num_heads, nsplit) splits (the
+ * count run with TVMLA_FLAG_TUNE_NSPLIT), so one workspace serves both.
  *
  * Layout (each region 256-byte aligned), R = num_draft*num_heads, for the
  * nsplit a call uses:
@@ -131,12 +153,11 @@ size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads
  * mask_indptr   int32 [batch+1]
  * sm_scale      multiplies the full 576-wide dot product; must be finite
  *               and positive (a softmax temperature), else TVMLA_E_VALUE
- * nsplit        splits per request: split s covers keys
- *               [s*chunk, min((s+1)*chunk, N_b)), chunk = ceil(N_b/nsplit)
- *               (page 1, "The NSPLIT Calculation"); empty splits return at
- *               once. The call uses tvmla_effective_nsplit(...) splits: a
- *               fixed multiple of nsplit when the grid would otherwise
- *               leave compute units idle.
+ * nsplit        splits per request, used exactly as given: split s covers
+ *               keys [s*chunk, min((s+1)*chunk, N_b)), chunk =
+ *               ceil(N_b/nsplit) (page 1, "The NSPLIT Calculation"); empty
+ *               splits return at once. (tvmla_verify_ex with
+ *               TVMLA_FLAG_TUNE_NSPLIT adapts the count to the GPU.)
  * out      [batch*num_draft, num_heads, 512] dtype, contiguous; bf16 output
  *          is rounded to nearest even
  * lse      [batch*num_draft, num_heads] fp32, contiguous: natural log of the
@@ -160,7 +181,8 @@ tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t
                           size_t workspace_bytes, void* stream);
 
 /*
- * tvmla_verify with two extra knobs:
+ * tvmla_verify with four extra knobs (tvmla_verify is this call with
+ * TVMLA_ALGO_AUTO, 0, 0, -1):
  *   algo       a tvmla_algo value (TVMLA_ALGO_AUTO is tvmla_verify's choice)
  *   min_chunk  lower bound on the per-split chunk: chunk =
  *              max(ceil(N_b/nsplit), min_chunk). 0 or 1 keeps the rule
@@ -168,6 +190,8 @@ tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t
  *              longer splits (the launch is unchanged; surplus splits return
  *              at once), which cuts partial-result traffic; the result
  *              differs only by rounding.
+ *   flags      0 or TVMLA_FLAG_TUNE_NSPLIT (other bits: TVMLA_E_VALUE)
+ *   fold_log2  the fold threshold described above (negative: default)
  */
 tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
                              const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
@@ -176,7 +200,8 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
                              const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                              int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                              int32_t dtype, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk,
+                             uint32_t flags, float fold_log2);
 
 /*
  * tvmla_verify_ex for draft trees of different sizes per request: request b
@@ -204,16 +229,17 @@ tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, 
                                  const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
                                  int32_t batch, int32_t max_draft, int32_t num_heads, float sm_scale,
                                  int32_t nsplit, int32_t dtype, void* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk);
+                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk,
+                                 uint32_t flags, float fold_log2);
 
 /*
- * The split step alone: the same arguments as tvmla_verify_ex without out
- * and lse. It enqueues only the split kernel, which leaves every non-empty
- * split's partial result in the workspace (layout under
- * tvmla_workspace_bytes); tvmla_combine with the same kv_indptr, nsplit and
- * min_chunk then produces exactly what tvmla_verify_ex does. Callers that
- * merge partials from several sources, or that time the two steps apart,
- * use the pair.
+ * The split step alone: the same arguments as tvmla_verify_ex without out,
+ * lse and flags (nsplit is always used as given). It enqueues only the split
+ * kernel, which leaves every non-empty split's partial result in the
+ * workspace (layout under tvmla_workspace_bytes); tvmla_combine with the same
+ * kv_indptr, nsplit and min_chunk then produces exactly what tvmla_verify_ex
+ * does at that split count. Callers that merge partials from several
+ * sources, or that time the two steps apart, use the pair.
  */
 tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
                                    const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
@@ -222,7 +248,7 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
                                    const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                                    int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                                   int32_t algo, int32_t min_chunk);
+                                   int32_t algo, int32_t min_chunk, float fold_log2);
 
 /*
  * The combine step alone: merge per-split partials laid out as in
@@ -297,6 +323,48 @@ tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_d
 tvmla_status tvmla_tree_mask(const int32_t* parents, const int32_t* kv_indptr, int32_t batch, int32_t num_draft,
                              uint8_t* custom_mask, int32_t* mask_indptr, void* stream);
 
+/* Which array tvmla_check_metadata found at fault. */
+typedef enum {
+  TVMLA_META_NONE = 0,
+  TVMLA_META_KV_INDPTR = 1,
+  TVMLA_META_KV_INDICES = 2,
+  TVMLA_META_OUT_CACHE_LOC = 3,
+  TVMLA_META_MASK_INDPTR = 4,
+  TVMLA_META_QO_INDPTR = 5
+} tvmla_meta_array;
+
+/*
+ * Host-side check of the metadata a verify call reads raw (SGLang's
+ * metadata buffers, which the kernel consumes as they are: "The
+ * Architecture of Capture Safety: ...", section "The Core Problem"). All
+ * pointers here are HOST pointers (copies of what the device call will
+ * get); nothing is enqueued and no HIP call is made. Returns TVMLA_OK when
+ * every offset and slot a call with these arguments (tvmla_verify/_ex when
+ * qo_indptr is NULL, tvmla_verify_ragged with max_draft = num_draft
+ * otherwise) would read lies inside its array, else TVMLA_E_INDEX and, when
+ * the pointers are non-NULL, the faulty array (tvmla_meta_array) in
+ * *bad_array and the element position in *bad_pos (-1 if none). Checks, in
+ * this order:
+ *   kv_indptr   kv_indptr[0] >= 0; 0 <= P_b <= INT32_MAX - 64 (so N_b fits
+ *               32 bits); kv_indptr[batch] <= kv_indices_len
+ *   qo_indptr   (if given) qo_indptr[0] >= 0 and non-decreasing (a T_b above
+ *               num_draft is clamped, as the verify calls do)
+ *   kv_indices  every entry in [kv_indptr[0], kv_indptr[batch]) is a slot
+ *               in [0, num_slots)
+ *   per request b, in order: out_cache_loc positions of its T_b draft tokens
+ *               inside out_cache_loc_len and their slots in [0, num_slots);
+ *               then mask_indptr[b] >= 0 and mask_indptr[b] + T_b * N_b <=
+ *               mask_len
+ * Other errors: TVMLA_E_NULLPTR (kv_indptr, out_cache_loc, mask_indptr
+ * NULL, or kv_indices NULL with kv_indices_len > 0), TVMLA_E_SHAPE (batch
+ * outside [1, 65535], num_draft outside [1, 64], num_slots < 1, a negative
+ * length).
+ */
+tvmla_status tvmla_check_metadata(const int32_t* kv_indptr, const int32_t* kv_indices, int64_t kv_indices_len,
+                                  const int32_t* out_cache_loc, int64_t out_cache_loc_len, const int32_t* mask_indptr,
+                                  int64_t mask_len, const int64_t* qo_indptr, int32_t batch, int32_t num_draft,
+                                  int64_t num_slots, int32_t* bad_array, int64_t* bad_pos);
+
 /* A static, human-readable name for a status code (host pointer, never NULL). */
 const char* tvmla_status_str(int32_t status);
 
@@ -305,14 +373,16 @@ int32_t tvmla_version(void);
 
 /*
  * The algorithm TVMLA_ALGO_AUTO resolves to for these sizes and dtype (a
- * tvmla_algo value), or a negative tvmla_status for out-of-range sizes or
- * an unknown dtype. Host only; no HIP call.
+ * tvmla_algo value), nsplit being the split count the call runs (with
+ * TVMLA_FLAG_TUNE_NSPLIT, tvmla_effective_nsplit(...)), or a negative
+ * tvmla_status for out-of-range sizes or an unknown dtype. Host only; no
+ * HIP call.
  */
 int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit, int32_t dtype);
 
 /*
- * The split count the split+combine entry points (tvmla_verify, _ex,
- * _ragged) actually use for these sizes. With G = batch * nsplit *
+ * The split count tvmla_verify_ex and tvmla_verify_ragged run with
+ * TVMLA_FLAG_TUNE_NSPLIT for these sizes. With G = batch * nsplit *
  * ceil(num_draft * num_heads / 128) workgroups of the 128-row kernel:
  * nsplit doubled (up to TVMLA_MAX_NSPLIT) while G < 256, i.e. while the
  * requested grid would leave compute units idle (few rows per request, e.g.
@@ -322,9 +392,10 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
  * else nsplit halved while it is even and the halved grid still has >= 512
  * workgroups when batch <= 64 (at least two rounds: such batches are served
  * longest request first) or >= 1024 for larger batches (four rounds); fewer
- * partial rows to write and combine. A fixed function of the sizes, so a captured graph keeps its
- * grid; the workspace size from tvmla_workspace_bytes accounts for it.
- * tvmla_verify_partials and tvmla_combine use nsplit exactly as given.
+ * partial rows to write and combine. A fixed function of the sizes, so a
+ * captured graph keeps its grid; the workspace size from
+ * tvmla_workspace_bytes accounts for it. tvmla_verify, tvmla_verify_partials
+ * and tvmla_combine use nsplit exactly as given.
  * Negative tvmla_status for out-of-range sizes. Host only.
  */
 int32_t tvmla_effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit);

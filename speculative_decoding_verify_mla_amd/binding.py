@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(PKG, "libtvmla.so")
 
 BF16, FP32 = 0, 1
 ALGO_AUTO, ALGO_SCALAR, ALGO_MFMA, ALGO_ROWS = 0, 1, 2, 3
+TUNE_NSPLIT = 1  # TVMLA_FLAG_TUNE_NSPLIT
+FOLD_DEFAULT = -1.0  # fold_log2 < 0: the library's default threshold
+META_ARRAYS = {0: "none", 1: "kv_indptr", 2: "kv_indices", 3: "out_cache_loc", 4: "mask_indptr", 5: "qo_indptr"}
 D_LATENT, D_ROPE, D_KEY = 512, 64, 576
 
 STATUS = {
@@ -28,12 +31,13 @@ STATUS = {
     6: "TVMLA_E_LAUNCH",
     7: "TVMLA_E_ALGO",
     8: "TVMLA_E_VALUE",
+    9: "TVMLA_E_INDEX",
 }
 
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_ragged", "tvmla_verify_partials",
            "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version",
-           "tvmla_auto_algo", "tvmla_effective_nsplit")
+           "tvmla_auto_algo", "tvmla_effective_nsplit", "tvmla_check_metadata")
 
 
 class TvmlaError(RuntimeError):
@@ -44,7 +48,8 @@ class TvmlaError(RuntimeError):
 
 _lib = None
 
-_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_P, _I32, _U32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, ctypes.c_float,
+                                   ctypes.c_size_t)
 _VERIFY_ARGS = [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _I32, _I32,
                 _P, _P, _P, _SZ, _P]
 
@@ -63,11 +68,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_workspace_bytes.restype = _SZ
     lib.tvmla_verify.argtypes = _VERIFY_ARGS
     lib.tvmla_verify.restype = ctypes.c_int
-    lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32]
+    lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_ex.restype = ctypes.c_int
-    lib.tvmla_verify_ragged.argtypes = _VERIFY_ARGS[:13] + [_P] + _VERIFY_ARGS[13:] + [_I32, _I32]
+    lib.tvmla_verify_ragged.argtypes = _VERIFY_ARGS[:13] + [_P] + _VERIFY_ARGS[13:] + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_ragged.restype = ctypes.c_int
-    lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32]
+    lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32, _F32]
     lib.tvmla_verify_partials.restype = ctypes.c_int
     lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
     lib.tvmla_combine.restype = ctypes.c_int
@@ -83,6 +88,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_auto_algo.restype = _I32
     lib.tvmla_effective_nsplit.argtypes = [_I32] * 4
     lib.tvmla_effective_nsplit.restype = _I32
+    lib.tvmla_check_metadata.argtypes = [_P, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I64, _P, _P]
+    lib.tvmla_check_metadata.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -150,21 +157,27 @@ def _verify_args(q_nope, q_rope, kv_cache, num_draft):
     return ntok // num_draft, H, dt
 
 
+def _out_args(q_nope, out, lse):
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise TvmlaError(5, "out and lse must be contiguous")
+    if out.dtype != q_nope.dtype:
+        raise TvmlaError(3, "out must have q's dtype")
+
+
 def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
            sm_scale: float, nsplit: int, out, lse, workspace, num_draft: int,
-           algo: int = ALGO_AUTO, min_chunk: int = 0, stream=None) -> None:
+           algo: int = ALGO_AUTO, min_chunk: int = 0, flags: int = 0, fold_log2: float = FOLD_DEFAULT,
+           stream=None) -> None:
     """Enqueue tvmla_verify_ex on `stream` (default: torch's current stream).
 
     q_nope [batch*T, H, 512], q_rope [batch*T, H, 64] (last dim contiguous),
     kv_cache [slots, >=576] (row-contiguous), int32 metadata, uint8 mask,
     out [batch*T, H, 512] (q's dtype), lse [batch*T, H] fp32, workspace a
-    tensor of at least workspace_bytes(...) bytes.
+    tensor of at least workspace_bytes(...) bytes. flags = TUNE_NSPLIT runs
+    effective_nsplit(...) splits instead of exactly nsplit.
     """
     batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
-    if not (out.is_contiguous() and lse.is_contiguous()):
-        raise TvmlaError(5, "out and lse must be contiguous")
-    if out.dtype != q_nope.dtype:
-        raise TvmlaError(3, "out must have q's dtype")
+    _out_args(q_nope, out, lse)
     st = load().tvmla_verify_ex(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
@@ -172,13 +185,31 @@ def verify(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custo
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         batch, num_draft, H, float(sm_scale), nsplit, dt,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream_ptr(stream), algo, min_chunk)
+        _stream_ptr(stream), algo, min_chunk, flags, float(fold_log2))
+    _check(st)
+
+
+def verify_plain(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                 sm_scale: float, nsplit: int, out, lse, workspace, num_draft: int, stream=None) -> None:
+    """Enqueue tvmla_verify itself (the pages' call: exactly nsplit splits,
+    automatic kernel choice); same tensors as verify()."""
+    batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
+    _out_args(q_nope, out, lse)
+    st = load().tvmla_verify(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0),
+        _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
+        batch, num_draft, H, float(sm_scale), nsplit, dt,
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream))
     _check(st)
 
 
 def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                   qo_indptr, sm_scale: float, nsplit: int, out, lse, workspace, max_draft: int,
-                  algo: int = ALGO_AUTO, min_chunk: int = 0, stream=None) -> None:
+                  algo: int = ALGO_AUTO, min_chunk: int = 0, flags: int = 0, fold_log2: float = FOLD_DEFAULT,
+                  stream=None) -> None:
     """Enqueue tvmla_verify_ragged: request b has qo_indptr[b+1] - qo_indptr[b]
     draft tokens (at most max_draft); q/out/lse hold qo_indptr[batch] token rows."""
     ntok, H, dl = q_nope.shape
@@ -199,13 +230,13 @@ def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         _ptr(qo_indptr), batch, max_draft, H, float(sm_scale), nsplit, dt,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream_ptr(stream), algo, min_chunk)
+        _stream_ptr(stream), algo, min_chunk, flags, float(fold_log2))
     _check(st)
 
 
 def verify_partials(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                     sm_scale: float, nsplit: int, workspace, num_draft: int, algo: int = ALGO_AUTO,
-                    min_chunk: int = 0, stream=None) -> None:
+                    min_chunk: int = 0, fold_log2: float = FOLD_DEFAULT, stream=None) -> None:
     """Enqueue tvmla_verify_partials: the split step only (partials land in workspace)."""
     batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
     st = load().tvmla_verify_partials(
@@ -215,7 +246,7 @@ def verify_partials(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_l
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         batch, num_draft, H, float(sm_scale), nsplit, dt,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream_ptr(stream), algo, min_chunk)
+        _stream_ptr(stream), algo, min_chunk, float(fold_log2))
     _check(st)
 
 
@@ -269,3 +300,28 @@ def tree_mask(parents, kv_indptr, num_draft: int, custom_mask, mask_indptr, stre
     st = load().tvmla_tree_mask(_ptr(parents), _ptr(kv_indptr), batch, num_draft, _ptr(custom_mask),
                                 _ptr(mask_indptr), _stream_ptr(stream))
     _check(st)
+
+
+def check_metadata(kv_indptr, kv_indices, out_cache_loc, mask_indptr, mask_len: int, num_draft: int,
+                   num_slots: int, qo_indptr=None):
+    """Run tvmla_check_metadata on host copies of the metadata (numpy arrays
+    or CPU tensors; int32, qo_indptr int64). Returns (status, array name,
+    position): status 0 when every offset and slot is in range."""
+    import numpy as np
+
+    def host(a, dt):
+        if a is None:
+            return None
+        if hasattr(a, "detach"):
+            a = a.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(a), dtype=dt)
+
+    ip, idx, ocl, mi = host(kv_indptr, np.int32), host(kv_indices, np.int32), host(out_cache_loc, np.int32), \
+        host(mask_indptr, np.int32)
+    qo = host(qo_indptr, np.int64)
+    bad_array, bad_pos = ctypes.c_int32(-7), ctypes.c_int64(-7)
+    st = load().tvmla_check_metadata(ip.ctypes.data, idx.ctypes.data if idx.size else None, idx.size,
+                                     ocl.ctypes.data, ocl.size, mi.ctypes.data, int(mask_len),
+                                     None if qo is None else qo.ctypes.data, ip.size - 1, num_draft, int(num_slots),
+                                     ctypes.byref(bad_array), ctypes.byref(bad_pos))
+    return st, META_ARRAYS.get(bad_array.value, bad_array.value), bad_pos.value

@@ -77,21 +77,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
-    build_probe(verbose)
     return LIB
-
-
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
-PROBE_LIB = os.path.join(PKG, "libtvmla_probe.so")
-
-
-def build_probe(verbose: bool = False) -> str:
-    """The matrix-core throughput probe bench.py runs beside the verify call
-    (not part of libtvmla.so)."""
-    tmp = PROBE_LIB + ".tmp"
-    _run([HIPCC, *CFLAGS, "-shared", "-o", tmp, PROBE_SRC], verbose)
-    os.replace(tmp, PROBE_LIB)
-    return PROBE_LIB
 
 
 if __name__ == "__main__":

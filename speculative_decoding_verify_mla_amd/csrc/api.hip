@@ -11,7 +11,8 @@
 #include "../../include/tvmla.h"
 #include "tvmla_internal.h"
 
-#include <stdlib.h>
+#include <algorithm>
+#include <climits>
 
 using namespace tvmla;
 
@@ -28,21 +29,12 @@ tvmla_status check_shape(int32_t batch, int32_t num_draft, int32_t num_heads, in
 }
 
 // Growth of a row's running max (log2 units) past which the row-owner
-// kernel folds its accumulator into the workspace (16: probabilities stay
-// below 2^16). TVMLA_FOLD_LOG2 overrides it, read at every call; results are
-// the same for any value >= 0, only the number of folds changes, which lets
-// tests drive the fold path on ordinary data.
-float fold_log2() {
-  const char* env = getenv("TVMLA_FOLD_LOG2");
-  if (env && *env) {
-    char* endp = nullptr;
-    const float v = strtof(env, &endp);
-    if (endp != env && v >= 0.f && v < INFINITY) return v;
-  }
-  return 16.f;
-}
+// kernel folds its accumulator into the workspace: 16 (probabilities stay
+// below 2^16) unless the caller passes a threshold >= 0. Results are the same
+// for any threshold; only the number of folds changes.
+float fold_threshold(float fold_log2) { return fold_log2 >= 0.f && fold_log2 < INFINITY ? fold_log2 : 16.f; }
 
-// Splits the split+combine entry points use: the caller's nsplit doubled
+// Splits the split+combine entry points run with TVMLA_FLAG_TUNE_NSPLIT: the caller's nsplit doubled
 // (up to TVMLA_MAX_NSPLIT) while the 128-row grid, batch * nsplit * ceil(T*H
 // / 128) workgroups, would not cover the 256 compute units -- the shapes with
 // few rows per request (8 heads per GPU) -- else halved as described below.
@@ -104,7 +96,8 @@ const char* tvmla_status_str(int32_t status) {
     case TVMLA_E_ALIGN: return "pointer or stride misaligned";
     case TVMLA_E_LAUNCH: return "kernel launch failed";
     case TVMLA_E_ALGO: return "unknown algorithm";
-    case TVMLA_E_VALUE: return "sm_scale must be finite and positive";
+    case TVMLA_E_VALUE: return "a value argument is out of range (sm_scale, flags or fold threshold)";
+    case TVMLA_E_INDEX: return "metadata holds an offset or slot out of range";
     default: return "unknown status";
   }
 }
@@ -115,8 +108,7 @@ int32_t tvmla_auto_algo(int32_t batch, int32_t num_draft, int32_t num_heads, int
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return -TVMLA_E_DTYPE;
   const tvmla_status st = check_shape(batch, num_draft, num_heads, nsplit);
   if (st != TVMLA_OK) return -st;
-  return dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, effective_nsplit(batch, num_draft, num_heads, nsplit))
-                             : TVMLA_ALGO_SCALAR;
+  return dtype == TVMLA_BF16 ? auto_bf16(batch, num_draft, num_heads, nsplit) : TVMLA_ALGO_SCALAR;
 }
 
 int32_t tvmla_effective_nsplit(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
@@ -134,7 +126,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
                             const int32_t* mask_indptr, int32_t batch, int32_t num_draft, int32_t num_heads,
                             float sm_scale, int32_t nsplit, int32_t dtype, const void* out, const float* lse,
                             bool need_out, void* workspace, size_t workspace_bytes, int32_t& algo,
-                            int32_t min_chunk, SplitParams& p) {
+                            int32_t min_chunk, float fold_log2, SplitParams& p) {
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
   if (algo != TVMLA_ALGO_AUTO && algo != TVMLA_ALGO_SCALAR && algo != TVMLA_ALGO_MFMA && algo != TVMLA_ALGO_ROWS)
     return TVMLA_E_ALGO;
@@ -149,6 +141,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   if (st != TVMLA_OK) return st;
   if (min_chunk < 0) return TVMLA_E_SHAPE;
   if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return TVMLA_E_VALUE;
+  if (fold_log2 != fold_log2) return TVMLA_E_VALUE;  // NaN
   if (kv_stride_row < TVMLA_D_KEY) return TVMLA_E_SHAPE;
   if (q_nope_stride_tok < 0 || q_nope_stride_head < 0 || q_rope_stride_tok < 0 || q_rope_stride_head < 0)
     return TVMLA_E_SHAPE;
@@ -185,7 +178,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
   p.lse_part = reinterpret_cast<float*>(ws + wl.lse_off);
   p.qo_indptr = nullptr;
-  p.fold_log2 = fold_log2();
+  p.fold_log2 = fold_threshold(fold_log2);
   return TVMLA_OK;
 }
 
@@ -196,7 +189,9 @@ static hipError_t launch_split(const SplitParams& p, int32_t algo, int32_t dtype
   return launch_split_scalar_fp32(p, s);
 }
 
-// Split + combine; qo_indptr null = num_draft tokens per request.
+// Split + combine; qo_indptr null = num_draft tokens per request. With
+// TVMLA_FLAG_TUNE_NSPLIT the call runs effective_nsplit(...) splits, else
+// exactly nsplit.
 static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
                                 const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
                                 const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
@@ -204,13 +199,14 @@ static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, i
                                 const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
                                 int32_t batch, int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                 int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream, int32_t algo, int32_t min_chunk) {
+                                void* stream, int32_t algo, int32_t min_chunk, uint32_t flags, float fold_log2) {
+  if (flags & ~(uint32_t)TVMLA_FLAG_TUNE_NSPLIT) return TVMLA_E_VALUE;
   SplitParams p;
-  nsplit = effective_nsplit(batch, num_draft, num_heads, nsplit);
+  if (flags & TVMLA_FLAG_TUNE_NSPLIT) nsplit = effective_nsplit(batch, num_draft, num_heads, nsplit);
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
                             q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
                             custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse,
-                            true, workspace, workspace_bytes, algo, min_chunk, p);
+                            true, workspace, workspace_bytes, algo, min_chunk, fold_log2, p);
   if (st != TVMLA_OK) return st;
   p.qo_indptr = qo_indptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -239,11 +235,12 @@ tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int6
                              const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                              int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                              int32_t dtype, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+                             size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk,
+                             uint32_t flags, float fold_log2) {
   return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
                      kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                      nullptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
-                     workspace_bytes, stream, algo, min_chunk);
+                     workspace_bytes, stream, algo, min_chunk, flags, fold_log2);
 }
 
 tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
@@ -253,12 +250,13 @@ tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, 
                                  const uint8_t* custom_mask, const int32_t* mask_indptr, const int64_t* qo_indptr,
                                  int32_t batch, int32_t max_draft, int32_t num_heads, float sm_scale,
                                  int32_t nsplit, int32_t dtype, void* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk) {
+                                 size_t workspace_bytes, void* stream, int32_t algo, int32_t min_chunk,
+                                 uint32_t flags, float fold_log2) {
   if (!qo_indptr) return TVMLA_E_NULLPTR;
   return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
                      kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                      qo_indptr, batch, max_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
-                     workspace_bytes, stream, algo, min_chunk);
+                     workspace_bytes, stream, algo, min_chunk, flags, fold_log2);
 }
 
 tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
@@ -268,12 +266,12 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
                                    const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                                    int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                                   int32_t algo, int32_t min_chunk) {
+                                   int32_t algo, int32_t min_chunk, float fold_log2) {
   SplitParams p;
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
                             q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
                             custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, nullptr,
-                            nullptr, false, workspace, workspace_bytes, algo, min_chunk, p);
+                            nullptr, false, workspace, workspace_bytes, algo, min_chunk, fold_log2, p);
   if (st != TVMLA_OK) return st;
   if (launch_split(p, algo, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
   return TVMLA_OK;
@@ -287,10 +285,10 @@ tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t
                           int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                           int32_t dtype, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return tvmla_verify_ex(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
-                         q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
-                         custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out,
-                         lse, workspace, workspace_bytes, stream, TVMLA_ALGO_AUTO, 0);
+  return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
+                     kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                     nullptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
+                     workspace_bytes, stream, TVMLA_ALGO_AUTO, 0, 0u, -1.f);
 }
 
 tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,
@@ -319,6 +317,53 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
   c.out = out;
   c.lse = lse;
   if (launch_combine(c, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
+  return TVMLA_OK;
+}
+
+tvmla_status tvmla_check_metadata(const int32_t* kv_indptr, const int32_t* kv_indices, int64_t kv_indices_len,
+                                  const int32_t* out_cache_loc, int64_t out_cache_loc_len, const int32_t* mask_indptr,
+                                  int64_t mask_len, const int64_t* qo_indptr, int32_t batch, int32_t num_draft,
+                                  int64_t num_slots, int32_t* bad_array, int64_t* bad_pos) {
+  auto fail = [&](int32_t array, int64_t pos) {
+    if (bad_array) *bad_array = array;
+    if (bad_pos) *bad_pos = pos;
+    return TVMLA_E_INDEX;
+  };
+  if (bad_array) *bad_array = TVMLA_META_NONE;
+  if (bad_pos) *bad_pos = -1;
+  if (!kv_indptr || !out_cache_loc || !mask_indptr || (!kv_indices && kv_indices_len > 0)) return TVMLA_E_NULLPTR;
+  if (batch < 1 || batch > 65535 || num_draft < 1 || num_draft > TVMLA_MAX_DRAFT) return TVMLA_E_SHAPE;
+  if (num_slots < 1 || kv_indices_len < 0 || out_cache_loc_len < 0 || mask_len < 0) return TVMLA_E_SHAPE;
+  // offsets: kv_indptr non-decreasing inside kv_indices, prefixes short
+  // enough that N_b = P_b + T_b fits the kernels' 32-bit key positions
+  if (kv_indptr[0] < 0) return fail(TVMLA_META_KV_INDPTR, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t P = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+    if (P < 0 || P > INT32_MAX - TVMLA_MAX_DRAFT) return fail(TVMLA_META_KV_INDPTR, b + 1);
+  }
+  if (kv_indptr[batch] > kv_indices_len) return fail(TVMLA_META_KV_INDPTR, batch);
+  if (qo_indptr) {
+    if (qo_indptr[0] < 0) return fail(TVMLA_META_QO_INDPTR, 0);
+    for (int32_t b = 0; b < batch; ++b)
+      if (qo_indptr[b + 1] < qo_indptr[b]) return fail(TVMLA_META_QO_INDPTR, b + 1);
+  }
+  // slots
+  for (int64_t j = kv_indptr[0]; j < kv_indptr[batch]; ++j)
+    if (kv_indices[j] < 0 || kv_indices[j] >= num_slots) return fail(TVMLA_META_KV_INDICES, j);
+  for (int32_t b = 0; b < batch; ++b) {
+    int64_t t0 = (int64_t)b * num_draft, Tb = num_draft;
+    if (qo_indptr) {  // the kernels clamp a request's token count to num_draft
+      t0 = qo_indptr[b];
+      Tb = std::min<int64_t>(qo_indptr[b + 1] - t0, num_draft);
+    }
+    for (int64_t t = t0; t < t0 + Tb; ++t) {
+      if (t >= out_cache_loc_len) return fail(TVMLA_META_OUT_CACHE_LOC, t);
+      if (out_cache_loc[t] < 0 || out_cache_loc[t] >= num_slots) return fail(TVMLA_META_OUT_CACHE_LOC, t);
+    }
+    // the request's [T_b][N_b] mask block must lie inside custom_mask
+    const int64_t N = (int64_t)kv_indptr[b + 1] - kv_indptr[b] + Tb;
+    if (mask_indptr[b] < 0 || mask_indptr[b] + Tb * N > mask_len) return fail(TVMLA_META_MASK_INDPTR, b);
+  }
   return TVMLA_OK;
 }
 

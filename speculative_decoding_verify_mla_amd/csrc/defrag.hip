@@ -8,12 +8,13 @@
 // is the plan's last phase (same page, section "Output Knowledge Created").
 // Prefix position p of request b moves to slot dst_base[b] + p.
 //
-// Copy kernel: grid (gx, batch); workgroup x of request b copies rows
-// j = x, x + gx, x + 2gx, ... of that request, flattened with their 16-byte
-// chunks over the 256 threads (72 chunks per bf16 row, 144 per fp32 row), so
-// each row is read and written as contiguous 16-byte pieces. Four pieces per
-// thread are in flight at once. HBM-bound: per row 2 x 576 x elem_size bytes
-// plus the 4-byte index.
+// Copy kernel: grid (gx, batch). A wavefront copies 8 consecutive prefix
+// rows of request b at a time (units u = wavefront id, + stride, ...): lanes
+// 0..7 load the 8 rows' slots, then the 8 x 72 16-byte chunks of the rows
+// (8 x 144 for fp32) are spread over the 64 lanes, 9 (18) per lane, all
+// loads issued before the first store. Each row is read and written as
+// contiguous 16-byte pieces; the chunk values stay in registers. HBM-bound:
+// per row 2 x 576 x elem_size bytes plus the 4-byte index.
 //
 // Index kernel: kv_indices_out[kv_indptr[b] + j] = dst_base[b] + j. It runs
 // after the copy on the same stream, so kv_indices_out may alias kv_indices.
@@ -24,38 +25,51 @@ namespace tvmla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kInFlight = 4;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 8;  // rows per wavefront unit
+
+// Nine chunks of a unit, chunk ids id = lane + 64 (K0 + k), k = 0..8: all
+// nine loads first, then the stores (named registers, so nothing goes to
+// scratch or LDS). Chunks past the unit's last row re-read that row and are
+// not stored.
+template <int kChunks, int K0>
+__device__ __forceinline__ void copy_nine(const char* src, char* dst, const DefragParams& d, int64_t slot, int nr,
+                                          int64_t drow0, int lane) {
+#define TVMLA_CHUNK(k, r, c) \
+  const int id##k = lane + 64 * (K0 + k), r = id##k / kChunks, c = id##k - r * kChunks
+#define TVMLA_LOAD(k)                                                         \
+  TVMLA_CHUNK(k, r##k, c##k);                                                 \
+  const int64_t s##k = __shfl(slot, r##k < nr ? r##k : nr - 1, 64);          \
+  const uint4 v##k = *reinterpret_cast<const uint4*>(src + s##k * d.src_row_bytes + 16 * c##k)
+#define TVMLA_STORE(k) \
+  if (r##k < nr) *reinterpret_cast<uint4*>(dst + (drow0 + r##k) * d.dst_row_bytes + 16 * c##k) = v##k
+  TVMLA_LOAD(0); TVMLA_LOAD(1); TVMLA_LOAD(2); TVMLA_LOAD(3); TVMLA_LOAD(4);
+  TVMLA_LOAD(5); TVMLA_LOAD(6); TVMLA_LOAD(7); TVMLA_LOAD(8);
+  TVMLA_STORE(0); TVMLA_STORE(1); TVMLA_STORE(2); TVMLA_STORE(3); TVMLA_STORE(4);
+  TVMLA_STORE(5); TVMLA_STORE(6); TVMLA_STORE(7); TVMLA_STORE(8);
+#undef TVMLA_STORE
+#undef TVMLA_LOAD
+#undef TVMLA_CHUNK
+}
 
 template <int kChunks>  // 16-byte chunks per row: 72 (bf16) or 144 (fp32)
 __global__ __launch_bounds__(kThreads) void defrag_copy_kernel(DefragParams d) {
+  static_assert(kRows * kChunks % (64 * 9) == 0, "a unit's chunks must come in nines per lane");
   const int b = blockIdx.y;
-  const int gx = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int i0 = d.kv_indptr[b];
   const int P = d.kv_indptr[b + 1] - i0;
-  const int nrow = P > (int)blockIdx.x ? (P - (int)blockIdx.x + gx - 1) / gx : 0;  // rows of this workgroup
-  const int64_t items = (int64_t)nrow * kChunks;
+  const int units = (P + kRows - 1) / kRows;
   const int64_t dbase = d.dst_base[b];
   const char* src = static_cast<const char*>(d.src);
   char* dst = static_cast<char*>(d.dst);
-  for (int64_t w0 = threadIdx.x; w0 < items; w0 += (int64_t)kThreads * kInFlight) {
-    uint4 v[kInFlight];
-    int64_t doff[kInFlight];
-#pragma unroll
-    for (int u = 0; u < kInFlight; ++u) {
-      const int64_t w = w0 + (int64_t)u * kThreads;
-      doff[u] = -1;
-      if (w < items) {
-        const int i = (int)(w / kChunks);
-        const int c = (int)(w - (int64_t)i * kChunks);
-        const int j = (int)blockIdx.x + i * gx;
-        const int64_t slot = d.kv_indices[i0 + j];
-        v[u] = *reinterpret_cast<const uint4*>(src + slot * d.src_row_bytes + 16 * c);
-        doff[u] = (dbase + j) * d.dst_row_bytes + 16 * c;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kInFlight; ++u)
-      if (doff[u] >= 0) *reinterpret_cast<uint4*>(dst + doff[u]) = v[u];
+  for (int u = blockIdx.x * kWaves + wave; u < units; u += gridDim.x * kWaves) {
+    const int j0 = u * kRows;
+    const int nr = P - j0 < kRows ? P - j0 : kRows;  // rows of this unit (the request's last may be short)
+    const int64_t slot = lane < nr ? (int64_t)d.kv_indices[i0 + j0 + lane] : 0;
+    copy_nine<kChunks, 0>(src, dst, d, slot, nr, dbase + j0, lane);
+    if constexpr (kRows * kChunks == 2 * 64 * 9) copy_nine<kChunks, 9>(src, dst, d, slot, nr, dbase + j0, lane);
   }
 }
 
@@ -70,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void defrag_index_kernel(DefragParams d) 
 }  // namespace
 
 hipError_t launch_defrag(const DefragParams& d, int elem_size, hipStream_t stream) {
-  // about 2048 copy workgroups in all, at least one per request
+  // about 2048 copy workgroups (8,192 wavefronts) in all, at least one per request
   const unsigned gx = (unsigned)std::max(1, std::min(2048, (2048 + d.batch - 1) / d.batch));
   DefragParams arg = d;
   void* args[] = {&arg};

@@ -10,10 +10,19 @@ from speculative_decoding_verify_mla_amd import binding
 
 # bf16 outputs: |gpu - oracle| <= 2e-2 + 2e-2 |oracle|; fp32 lse: 1e-3 absolute.
 BF16_ATOL, BF16_RTOL, BF16_LSE = 2e-2, 2e-2, 1e-3
+# ... and ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3 over the compared outputs.
+# At long contexts |out| shrinks to ~0.075, so the 2e-2 absolute floor is a
+# third of a typical output and the element-wise bound alone would pass a
+# kernel that drops or mis-weights a fraction of the keys; the relative L2
+# error cannot hide that. A correct bf16 kernel sits near 2e-3: the bf16
+# rounding of the output (relative 2^-9 at most, ~1.1e-3 rms), of the
+# probabilities fed to the value product and of the split partials.
+BF16_REL_L2 = 5e-3
 # fp32 outputs: fp32 accumulation of 576-term dot products and of the softmax
 # sum keeps errors near 1e-6; 1e-4 leaves a wide margin and still catches any
 # dropped term or wrong index.
 FP32_ATOL, FP32_RTOL, FP32_LSE = 1e-4, 1e-4, 1e-4
+FP32_REL_L2 = 1e-5  # fp32 kernels measure ~2e-7
 
 
 def log(msg: str):
@@ -43,7 +52,8 @@ class Device:
         nbytes = binding.workspace_bytes(w.batch, w.num_draft, H, self.nsplit)
         self.ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=dev)
 
-    def run(self, algo=binding.ALGO_AUTO, min_chunk=0, nsplit=None, stream=None):
+    def run(self, algo=binding.ALGO_AUTO, min_chunk=0, nsplit=None, stream=None, flags=0,
+            fold_log2=binding.FOLD_DEFAULT):
         ns = nsplit or self.nsplit
         if ns != self.nsplit:
             nbytes = binding.workspace_bytes(self.w.batch, self.w.num_draft, self.w.num_heads, ns)
@@ -52,7 +62,7 @@ class Device:
         binding.verify(self.q_nope, self.q_rope, self.pool[:, :576] if self.pool.shape[1] != 576 else self.pool,
                        self.kv_indptr, self.kv_indices, self.out_cache_loc, self.custom_mask, self.mask_indptr,
                        self.w.sm_scale, ns, self.out, self.lse, self.ws, self.w.num_draft, algo=algo,
-                       min_chunk=min_chunk, stream=stream)
+                       min_chunk=min_chunk, flags=flags, fold_log2=fold_log2, stream=stream)
         return self.out, self.lse
 
     def result(self, **kw):
@@ -68,7 +78,8 @@ def tolerances(w):
 
 
 def compare(w, out, lse, ref_out, ref_lse, what=""):
-    """Element-wise check against the oracle; also logs max-abs, max-rel, rel-L2."""
+    """Element-wise check against the oracle, plus the relative L2 error of
+    the outputs; logs max-abs, worst error/bound, lse error and rel-L2."""
     atol, rtol, ltol = tolerances(w)
     err = np.abs(out - ref_out)
     bound = atol + rtol * np.abs(ref_out)
@@ -83,4 +94,6 @@ def compare(w, out, lse, ref_out, ref_lse, what=""):
     assert same_inf.all(), f"{what}: -inf lse pattern differs"
     fin = np.isfinite(ref_lse)
     assert np.all(lerr[fin] <= ltol), f"{what}: lse max err {lerr[fin].max()}"
+    l2_bound = BF16_REL_L2 if w.spec.dtype == "bf16" else FP32_REL_L2
+    assert l2 <= l2_bound, f"{what}: relative L2 error {l2:.3e} above {l2_bound:.0e}"
     return l2

@@ -40,20 +40,22 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert binding.version() >= 100
-    for code in range(9):
+    for code in range(10):
         s = binding.status_str(code)
         assert isinstance(s, str) and s
     assert binding.status_str(99) == "unknown status"
 
 
 def test_auto_algo(lib):
-    # 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512 workgroups, run as 32 splits (one round
-    # of 256) -> the 128-row kernel
+    # nsplit is the count the call runs. 64 splits x 8 row groups of 128 (16 tokens x 64 heads): 512
+    # workgroups -> the 128-row kernel; so at the 32 splits TVMLA_FLAG_TUNE_NSPLIT runs (256 workgroups)
     assert binding.auto_algo(1, 16, 64, 64) == binding.ALGO_ROWS
-    # 16 tokens x 8 heads: one row group; NSPLIT 64 is raised to 256 splits (256 workgroups)
-    assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_ROWS
+    assert binding.auto_algo(1, 16, 64, 32) == binding.ALGO_ROWS
+    # 16 tokens x 8 heads: one row group; 64 splits leave 192 CUs idle -> the 64-row kernel (128 workgroups)
+    assert binding.auto_algo(1, 16, 8, 64) == binding.ALGO_MFMA
+    # ... the 256 splits the tuned call runs fill them -> the 128-row kernel
+    assert binding.auto_algo(1, 16, 8, 256) == binding.ALGO_ROWS
     assert binding.auto_algo(4, 16, 8, 64) == binding.ALGO_ROWS
-    # 200 splits cannot double within 256: 200 workgroups of 128 rows -> the 64-row kernel
     assert binding.auto_algo(1, 16, 8, 200) == binding.ALGO_MFMA
     assert binding.auto_algo(1, 4, 64, 64, binding.FP32) == binding.ALGO_SCALAR
     assert binding.auto_algo(0, 4, 64, 64) == -2
@@ -110,7 +112,7 @@ def _call(lib, **kw):
     a = dict(q_nope=_FAKE, qn_st=64 * 512, qn_sh=512, q_rope=_FAKE, qr_st=64 * 64, qr_sh=64, kv=_FAKE,
              kv_stride=576, kv_indptr=_FAKE, kv_indices=_FAKE, ocl=_FAKE, mask=_FAKE, mask_indptr=_FAKE,
              batch=1, T=4, H=64, scale=0.07, nsplit=64, dtype=binding.BF16, out=_FAKE, lse=_FAKE,
-             ws=_FAKE, ws_bytes=None, stream=None, algo=0, min_chunk=0)
+             ws=_FAKE, ws_bytes=None, stream=None, algo=0, min_chunk=0, flags=0, fold=-1.0)
     a.update(kw)
     if a["ws_bytes"] is None:
         a["ws_bytes"] = binding.workspace_bytes(max(a["batch"], 1), max(min(a["T"], 64), 1),
@@ -119,7 +121,7 @@ def _call(lib, **kw):
                                a["kv_stride"], a["kv_indptr"], a["kv_indices"], a["ocl"], a["mask"],
                                a["mask_indptr"], a["batch"], a["T"], a["H"], a["scale"], a["nsplit"], a["dtype"],
                                a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"], a["algo"],
-                               a["min_chunk"])
+                               a["min_chunk"], a["flags"], a["fold"])
 
 
 @pytest.mark.parametrize("field", ["q_nope", "q_rope", "kv", "kv_indptr", "kv_indices", "ocl", "mask",
@@ -154,45 +156,78 @@ def test_bad_scale(lib, scale):
     assert _call(lib, scale=scale) == 8
 
 
+@pytest.mark.parametrize("kw", [dict(flags=2), dict(flags=0xFFFFFFFF), dict(flags=3), dict(fold=float("nan"))])
+def test_bad_flags_and_fold(lib, kw):
+    assert _call(lib, **kw) == 8
+
+
 @pytest.mark.parametrize("kw", [dict(q_nope=_FAKE + 8), dict(kv=_FAKE + 2), dict(out=_FAKE + 4), dict(ws=_FAKE + 8),
                                 dict(kv_stride=580), dict(qn_sh=516), dict(qr_st=64 * 64 + 4)])
 def test_misaligned(lib, kw):
     assert _call(lib, **kw) == 5
 
 
-def test_effective_nsplit_sweep(lib):
-    """The library's split count against the rule as its header states it,
-    over a grid of sizes (host-only call, no GPU needed)."""
+def test_effective_nsplit_properties(lib):
+    """Over a grid of sizes, the tuned split count has the properties it
+    exists for (host-only call, no GPU needed): it stays in 1..256 and is the
+    caller's count times or divided by a power of two; a raised count is the
+    smallest doubling whose 128-row grid covers the 256 compute units (or
+    the largest within 256); a lowered one keeps at least one round of 256
+    workgroups, and at least two rounds (batches up to 64, served longest
+    request first) or four (larger batches) unless the caller's grid had at
+    most two rounds; an unchanged count could not be halved under those
+    rules."""
 
-    def stated(batch, T, H, ns):
-        groups = -(-(T * H) // 128)
-        grid = lambda n: batch * n * groups
-        e = ns
-        while grid(e) < 256 and 2 * e <= 256:
-            e *= 2
-        if e != ns:
-            return e
-        if 256 < grid(e) <= 512:
-            return e // 2 if e % 2 == 0 and grid(e // 2) >= 256 else e
-        keep = 512 if batch <= 64 else 1024
-        while e % 2 == 0 and grid(e // 2) >= keep:
-            e //= 2
-        return e
+    def grid(batch, T, H, n):
+        return batch * n * -(-(T * H) // 128)
 
     n = 0
     for batch in (1, 2, 3, 7, 32, 64, 65, 300):
         for T, H in ((1, 1), (4, 8), (5, 8), (16, 8), (16, 64), (8, 64), (32, 64), (64, 128)):
             for ns in (1, 3, 7, 8, 32, 48, 63, 64, 128, 200, 256):
-                got = binding.effective_nsplit(batch, T, H, ns)
-                assert got == stated(batch, T, H, ns), (batch, T, H, ns, got)
-                assert 1 <= got <= 256
+                e = binding.effective_nsplit(batch, T, H, ns)
+                g = lambda k: grid(batch, T, H, k)
+                case = (batch, T, H, ns, e)
+                assert 1 <= e <= 256, case
+                ratio = e / ns if e >= ns else ns / e
+                assert ratio == int(ratio) and int(ratio) & (int(ratio) - 1) == 0, case
+                keep = 512 if batch <= 64 else 1024
+                if g(ns) < 256:
+                    # too few workgroups: doubled until the grid covers the CUs or 256 splits would be passed
+                    assert e >= ns and (g(e) >= 256 or 2 * e > 256), case
+                    assert e == ns or g(e // 2) < 256, case
+                elif e < ns:
+                    assert g(e) >= 256, case  # never leaves compute units idle
+                    if g(ns) <= 512:
+                        assert e * 2 == ns, case  # one round instead of two
+                    else:
+                        assert g(e) >= keep, case
+                        assert e % 2 == 1 or g(e // 2) < keep, case  # halved as far as allowed
+                else:
+                    assert e == ns, case
+                    if 256 < g(ns) <= 512:
+                        assert ns % 2 == 1 or g(ns // 2) < 256, case
+                    elif g(ns) > 512:
+                        assert ns % 2 == 1 or g(ns // 2) < keep, case
                 n += 1
     assert n == 8 * 8 * 11
 
 
+def _layout_bytes(batch, T, H, ns):
+    rows = batch * T * H * ns
+    o = (rows * 512 * 4 + 255) // 256 * 256
+    return o + (rows * 4 + 255) // 256 * 256
+
+
 def test_small_workspace(lib):
-    need = binding.workspace_bytes(1, 4, 64, 64)
+    # exactly nsplit splits: the workspace of 64 splits
+    need = _layout_bytes(1, 4, 64, 64)
+    assert binding.workspace_bytes(1, 4, 64, 64) >= need
     assert _call(lib, ws_bytes=need - 1) == 4
+    # tuned: 2 row groups x 64 splits = 128 workgroups, raised to 128 splits
+    assert binding.effective_nsplit(1, 4, 64, 64) == 128
+    assert binding.workspace_bytes(1, 4, 64, 64) == _layout_bytes(1, 4, 64, 128)
+    assert _call(lib, ws_bytes=_layout_bytes(1, 4, 64, 128) - 1, flags=binding.TUNE_NSPLIT) == 4
 
 
 def test_combine_errors(lib):
@@ -207,6 +242,19 @@ def test_combine_errors(lib):
     assert f(_FAKE + 4, ws, _FAKE, 2, 16, 64, 64, 0, 0, _FAKE, _FAKE, None) == 5
 
 
+def test_plain_verify_errors(lib):
+    """tvmla_verify (no algo, flags or fold arguments) runs the same host checks."""
+    f = lib.tvmla_verify
+    ws = _layout_bytes(1, 4, 64, 64)  # exactly the 64 splits the call runs
+    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 4, 64, 0.07,
+            64, binding.BF16, _FAKE, _FAKE, _FAKE, ws, None]
+    for idx, val, code in [(0, None, 1), (19, None, 1), (21, None, 4), (22, ws - 1, 4), (17, 257, 2), (18, 3, 3),
+                           (16, -1.0, 8), (6, _FAKE + 2, 5)]:
+        a = list(good)
+        a[idx] = val
+        assert f(*a) == code, (idx, val)
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(FileNotFoundError):
@@ -217,9 +265,9 @@ def test_partials_errors(lib):
     f = lib.tvmla_verify_partials
     ws = binding.workspace_bytes(2, 16, 64, 64)
     good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 16, 64, 0.07,
-            64, binding.BF16, _FAKE, ws, None, 0, 0]
+            64, binding.BF16, _FAKE, ws, None, 0, 0, -1.0]
     for idx, val, code in [(0, None, 1), (6, None, 1), (19, None, 4), (20, ws - 1, 4), (13, 0, 2), (18, 7, 3),
-                           (22, 9, 7), (7, 580, 5), (23, -1, 2)]:
+                           (22, 9, 7), (7, 580, 5), (23, -1, 2), (24, float("nan"), 8)]:
         a = list(good)
         a[idx] = val
         assert f(*a) == code, (idx, val)

@@ -110,8 +110,10 @@ def test_capture_ragged_verify():
         buf.qo_indptr.copy_(r.qo_indptr.cuda())
 
     def step():
+        # the tuned split count: a function of the sizes only, so the captured grid stays valid
         binding.verify_ragged(buf.q_nope, buf.q_rope, buf.pool, buf.kv_indptr, buf.kv_indices, buf.ocl, buf.mask,
-                              buf.mask_indptr, buf.qo_indptr, ws_list[0].sm_scale, NS, buf.out, buf.lse, buf.ws, T)
+                              buf.mask_indptr, buf.qo_indptr, ws_list[0].sm_scale, NS, buf.out, buf.lse, buf.ws, T,
+                              flags=binding.TUNE_NSPLIT)
 
     load(ws_list[0], rs[0])
     graph = _capture(step)

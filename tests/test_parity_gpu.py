@@ -1,8 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small and medium workloads are compared element by element on every output;
-the full-size long-context, ragged and heavy workloads on sampled rows the
-oracle computes one by one, plus properties that hold at any size.
+Every output is compared element by element (and by relative L2 error) with
+the oracle: the small and medium workloads, the full-size long-context,
+8-head and ragged workloads whole, and two whole requests of the heavy one
+(its other rows by properties that hold at any size: convex bounds and
+bitwise equality of the scattered and contiguous layouts).
 """
 import numpy as np
 import pytest
@@ -24,17 +26,11 @@ def _oracle(w, pool=None):
                      w.mask_indptr, w.sm_scale, w.num_draft)
 
 
-def _oracle_rows(w, picks, pool=None):
-    pool = w.host_pool() if pool is None else pool
-    return vo.verify_rows(w.q_nope, w.q_rope, pool, w.kv_indptr, w.kv_indices, w.out_cache_loc, w.custom_mask,
-                          w.mask_indptr, w.sm_scale, w.num_draft, picks)
-
-
-def _explicit(d, w, ns, algo):
-    """Split step + combine at exactly `ns` splits (the full call may raise a
-    small split count to fill the GPU; see effective_nsplit)."""
+def _explicit(d, w, ns, algo, fold_log2=binding.FOLD_DEFAULT):
+    """Split step + combine at exactly `ns` splits, through the two separate
+    entry points."""
     binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc, d.custom_mask,
-                            d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo)
+                            d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo, fold_log2=fold_log2)
     binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, ns, d.out, d.lse)
     torch.cuda.synchronize()
     return d.out.float().cpu().numpy().astype(np.float64), d.lse.cpu().numpy().astype(np.float64)
@@ -132,11 +128,11 @@ def test_nsplit_invariance(nsplit):
         compare(w, out, lse, ref_out, ref_lse, f"nsplit{nsplit}/algo{algo}")
 
 
-@pytest.mark.parametrize("fold", ["0", "0.5", "3"])
+@pytest.mark.parametrize("fold", [0.0, 0.5, 3.0])
 @pytest.mark.parametrize("name", ["ragged_h8", "groups_h64", "t64_h2", "chain_h16", "t2_h128"])
-def test_rows_fold_path(monkeypatch, fold, name):
+def test_rows_fold_path(fold, name):
     """The row-owner kernel folds its accumulator into the workspace when a
-    row's max outgrows its reference by more than TVMLA_FOLD_LOG2 (16 by
+    row's max outgrows its reference by more than 2^fold_log2 (16 by
     default, rare on these inputs). Thresholds of 0..3 make folds frequent,
     including repeated folds into the same slot; the result must not
     change."""
@@ -145,28 +141,24 @@ def test_rows_fold_path(monkeypatch, fold, name):
     for ns in (1, 2):  # long splits: folds need tiles after a row's first
         d = Device(w, nsplit=ns)
         base_out, base_lse = _explicit(d, w, ns, ROWS)
-        monkeypatch.setenv("TVMLA_FOLD_LOG2", fold)
         log(f"[{name}] nsplit {ns} fold threshold {fold}")
-        out, lse = _explicit(d, w, ns, ROWS)
-        monkeypatch.delenv("TVMLA_FOLD_LOG2")
+        out, lse = _explicit(d, w, ns, ROWS, fold_log2=fold)
         compare(w, out, lse, ref_out, ref_lse, f"{name}/nsplit{ns}/fold{fold}")
-        if fold == "0" and max(w.prefix_lens) + w.num_draft > 2 * 64 * ns:
+        if fold == 0.0 and max(w.prefix_lens) + w.num_draft > 2 * 64 * ns:
             # several tiles per split: the folds changed the rounding
             assert not np.array_equal(out, base_out), "no fold happened"
+        # the full call passes the threshold to the same kernel
+        o2, l2 = d.result(algo=ROWS, nsplit=ns, fold_log2=fold)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2)
 
 
 def test_rows_fold_one_split_long():
     """One split over 4,112 keys (65 tiles) with a fold on every growth of a
     row max: many folds per slot."""
-    import os
     w = gen.build("p4096")
     ref_out, ref_lse = _oracle(w)
     d = Device(w, nsplit=1)
-    os.environ["TVMLA_FOLD_LOG2"] = "0"
-    try:
-        out, lse = _explicit(d, w, 1, ROWS)
-    finally:
-        del os.environ["TVMLA_FOLD_LOG2"]
+    out, lse = _explicit(d, w, 1, ROWS, fold_log2=0.0)
     compare(w, out, lse, ref_out, ref_lse, "p4096/nsplit1/fold0")
 
 
@@ -193,7 +185,6 @@ def test_partials_match_oracle_splits():
     T, H = w.num_draft, w.num_heads
     for algo in (ROWS, MFMA, SCALAR):
         d.ws.fill_(float("nan"))
-        # the split step alone keeps nsplit as given (the full call may raise it; see effective_nsplit)
         binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
                                 d.custom_mask, d.mask_indptr, w.sm_scale, ns, d.ws, w.num_draft, algo=algo)
         torch.cuda.synchronize()
@@ -294,52 +285,103 @@ def test_masked_content_independence():
                 assert not np.array_equal(o1[rows], o2[rows])
 
 
-def _picks(w, per_request, seed=0):
-    rng = np.random.default_rng(seed)
-    T, H = w.num_draft, w.num_heads
-    picks = []
-    for b in range(w.batch):
-        cand = [(0, 0), (T - 1, H - 1)] + [(int(rng.integers(T)), int(rng.integers(H))) for _ in range(per_request)]
-        picks += [(b * T + i, h) for i, h in cand[:per_request]]
-    return picks
-
-
-def _convex_bounds(d, w, out):
+def _convex_bounds(w, out):
     """Each output entry is a convex combination of the visible values, so it
     lies within [min, max] of the request's 512 latent entries (any size)."""
     for b in range(w.batch):
-        lo_hi = []
         sl = slice(int(w.row_offsets[b]), int(w.row_offsets[b + 1]))
         rows = w.rows[sl][:, :512].cuda().float()
         lo, hi = rows.min(0).values, rows.max(0).values
         o = out[b * w.num_draft:(b + 1) * w.num_draft].float()
         slack = 2e-2 + 2e-2 * torch.maximum(lo.abs(), hi.abs())
         assert torch.all(o >= lo - slack) and torch.all(o <= hi + slack), b
-        del lo_hi
 
 
-@pytest.mark.parametrize("name,per_request", [("long185k", 24), ("ragged32", 2), ("heavy200k", 3)])
-def test_full_size_sampled(name, per_request):
+def _oracle_request(w, b, pool):
+    """The oracle on request b alone: the batch's arrays restricted to its
+    query rows, draft slots and its two offsets (kv_indptr and mask_indptr
+    keep their absolute values, so they still index the whole arrays)."""
+    T = w.num_draft
+    rows = slice(b * T, (b + 1) * T)
+    return vo.verify(w.q_nope[rows], w.q_rope[rows], pool, w.kv_indptr[b:b + 2], w.kv_indices,
+                     w.out_cache_loc[rows], w.custom_mask, w.mask_indptr[b:b + 2], w.sm_scale, T)
+
+
+def _both_calls(d, w):
+    """The pages' call (tvmla_verify: exactly the workload's NSPLIT, kernel
+    chosen automatically) and the tuned call (tvmla_verify_ex with
+    TVMLA_FLAG_TUNE_NSPLIT, the one bench.py times); yields (label, out, lse)
+    on the device."""
+    binding.verify_plain(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc, d.custom_mask,
+                         d.mask_indptr, w.sm_scale, d.nsplit, d.out, d.lse, d.ws, w.num_draft)
+    torch.cuda.synchronize()
+    yield f"tvmla_verify nsplit {d.nsplit}", d.out, d.lse
+    eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, d.nsplit)
+    d.out.fill_(float("nan"))
+    d.lse.fill_(float("nan"))
+    out, lse = d.run(flags=binding.TUNE_NSPLIT)
+    torch.cuda.synchronize()
+    yield f"tuned nsplit {d.nsplit}->{eff}", out, lse
+
+
+@pytest.mark.parametrize("name", ["long185k", "long185k_h8", "ragged32"])
+def test_full_size_whole(name):
+    """The full-size workloads, every output row against the oracle, through
+    both the pages' call and the tuned one."""
     w = gen.build(name)
-    log(f"[{name}] built: batch={w.batch} keys={w.total_keys}")
+    log(f"[{name}] built: batch={w.batch} keys={w.total_keys} rows={w.batch * w.num_draft * w.num_heads}")
     d = Device(w)
-    picks = _picks(w, per_request)
+    ref_out, ref_lse = _oracle(w)
+    log(f"[{name}] oracle done")
+    for label, out, lse in _both_calls(d, w):
+        _convex_bounds(w, out)
+        got_o = out.float().cpu().numpy().astype(np.float64)
+        got_l = lse.cpu().numpy().astype(np.float64)
+        compare(w, got_o, got_l, ref_out, ref_lse, f"{name} {label}, all rows")
+
+
+def test_full_size_heavy():
+    """heavy200k (8 requests x 200,000 prefix keys x 32 draft tokens x 64
+    heads): requests 0 and 7 whole against the oracle; every row within the
+    convex bounds; scattered and contiguous slots bit-identical."""
+    w = gen.build("heavy200k")
+    log(f"[heavy200k] built: batch={w.batch} keys={w.total_keys}")
+    d = Device(w)
     pool = w.host_pool()
-    ref_o, ref_l = _oracle_rows(w, picks, pool)
-    for algo in (ROWS, binding.ALGO_AUTO):
-        out, lse = d.run(algo=algo)
-        torch.cuda.synchronize()
-        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-        _convex_bounds(d, w, out)
-        got_o = np.stack([out[t, h].float().cpu().numpy() for t, h in picks]).astype(np.float64)
-        got_l = np.array([float(lse[t, h]) for t, h in picks])
-        compare(w, got_o, got_l, ref_o, ref_l, f"{name} algo{algo} sampled {len(picks)} rows")
-    if name == "heavy200k":
-        c = gen.build("heavy200k_contig")
-        dc = Device(c)
-        oc, lc = dc.run(algo=binding.ALGO_AUTO)
-        torch.cuda.synchronize()
-        assert torch.equal(out, oc) and torch.equal(lse, lc), "scattered and contiguous slots differ"
+    refs = {b: _oracle_request(w, b, pool) for b in (0, w.batch - 1)}
+    log("[heavy200k] oracle done for requests " + ", ".join(map(str, refs)))
+    T = w.num_draft
+    results = []
+    for label, out, lse in _both_calls(d, w):
+        _convex_bounds(w, out)
+        for b, (ro, rl) in refs.items():
+            go = out[b * T:(b + 1) * T].float().cpu().numpy().astype(np.float64)
+            gl = lse[b * T:(b + 1) * T].cpu().numpy().astype(np.float64)
+            compare(w, go, gl, ro, rl, f"heavy200k {label}, request {b} whole")
+        results.append((out.clone(), lse.clone()))
+    del d
+    c = gen.build("heavy200k_contig")
+    dc = Device(c)
+    for (o_s, l_s), (label, o_c, l_c) in zip(results, _both_calls(dc, c)):
+        assert torch.equal(o_s, o_c) and torch.equal(l_s, l_c), f"{label}: scattered and contiguous slots differ"
+
+
+@pytest.mark.parametrize("name", ["ragged_h8", "groups_h64", "t1_h1", "t64_h128", "fp32_ragged"])
+def test_plain_verify_entry_point(name):
+    """tvmla_verify itself (the pages' call, through ctypes): matches the
+    oracle and is bit-identical to tvmla_verify_ex with AUTO, no flags and
+    the default fold threshold."""
+    w = gen.build(SMALL[name])
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w)
+    binding.verify_plain(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc, d.custom_mask,
+                         d.mask_indptr, w.sm_scale, d.nsplit, d.out, d.lse, d.ws, w.num_draft)
+    torch.cuda.synchronize()
+    o1 = d.out.float().cpu().numpy().astype(np.float64)
+    l1 = d.lse.cpu().numpy().astype(np.float64)
+    compare(w, o1, l1, ref_out, ref_lse, f"{name}/tvmla_verify")
+    o2, l2 = d.result()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_graph_capture_replay():
@@ -397,8 +439,9 @@ def test_graph_capture_replay():
     ("groups4_h64", 64, 16),  # 4 requests x 8 row groups: 2048 workgroups, halved to 512 (two rounds)
 ])
 def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
-    """The full call runs the effective split count; it is bit-identical to
-    split + combine at that count, and matches the oracle."""
+    """With TVMLA_FLAG_TUNE_NSPLIT the call runs the effective split count;
+    it is bit-identical to split + combine at that count, and matches the
+    oracle."""
     spec = SMALL[name] if name in SMALL else gen.small(name, 4, [40, 300, 0, 129], 16, 64, seed=19)
     w = gen.build(spec)
     eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, ns)
@@ -406,7 +449,7 @@ def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
     ref_out, ref_lse = _oracle(w)
     d = Device(w, nsplit=ns)
     for algo in (binding.ALGO_AUTO, ROWS, MFMA):
-        o1, l1 = d.result(algo=algo)
+        o1, l1 = d.result(algo=algo, flags=binding.TUNE_NSPLIT)
         compare(w, o1, l1, ref_out, ref_lse, f"{name}/nsplit{ns}->{eff}/algo{algo}")
         binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
                                 d.custom_mask, d.mask_indptr, w.sm_scale, eff, d.ws, w.num_draft, algo=algo)
@@ -417,13 +460,14 @@ def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_partials_then_combine_equals_verify():
+@pytest.mark.parametrize("flags", [0, binding.TUNE_NSPLIT])
+def test_partials_then_combine_equals_verify(flags):
     w = gen.build(SMALL["groups_h64"])
     d = Device(w)
-    # the full call runs the effective split count; the two steps take it as given
-    ns = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, d.nsplit)
+    # the full call runs exactly nsplit splits, or the effective count when tuned; the two steps take it as given
+    ns = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, d.nsplit) if flags else d.nsplit
     for algo in (ROWS, MFMA, SCALAR):
-        o1, l1 = d.result(algo=algo)
+        o1, l1 = d.result(algo=algo, flags=flags)
         d.out.fill_(float("nan"))
         d.lse.fill_(float("nan"))
         d.ws.fill_(float("nan"))

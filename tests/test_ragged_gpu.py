@@ -13,7 +13,7 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, r, algo=binding.ALGO_AUTO, nsplit=None):
+def _run(w, r, algo=binding.ALGO_AUTO, nsplit=None, flags=0):
     dev = "cuda"
     ns = nsplit or w.spec.nsplit
     pool = w.device_pool(dev, fill=float("nan"))
@@ -28,7 +28,7 @@ def _run(w, r, algo=binding.ALGO_AUTO, nsplit=None):
     qn = r.q_nope.to(dev) if ntok else torch.zeros((1, H, 512), dtype=w.torch_dtype, device=dev)
     qr = r.q_rope.to(dev) if ntok else torch.zeros((1, H, 64), dtype=w.torch_dtype, device=dev)
     binding.verify_ragged(qn, qr, pool, w.kv_indptr.to(dev), kv_indices, ocl, mask, r.mask_indptr.to(dev),
-                          r.qo_indptr.to(dev), w.sm_scale, ns, out, lse, ws, w.num_draft, algo=algo)
+                          r.qo_indptr.to(dev), w.sm_scale, ns, out, lse, ws, w.num_draft, algo=algo, flags=flags)
     torch.cuda.synchronize()
     return out[:ntok].float().cpu().numpy().astype(np.float64), lse[:ntok].cpu().numpy().astype(np.float64)
 
@@ -62,12 +62,13 @@ def test_ragged_matches_oracle(name, algo):
     compare(w, out, lse, ref_o, ref_l, f"{name}/algo{algo}")
 
 
-def test_whole_trees_equal_fixed_verify():
+@pytest.mark.parametrize("flags", [0, binding.TUNE_NSPLIT])
+def test_whole_trees_equal_fixed_verify(flags):
     kw, _ = CASES["rag_bf16_h64"]
     w = gen.build(gen.small("rag_whole", **kw))
     r = gen.ragged_trees(w, [w.num_draft] * w.batch)
-    log("ragged case: whole trees vs tvmla_verify")
-    out, lse = _run(w, r)
+    log(f"ragged case: whole trees vs tvmla_verify, flags {flags}")
+    out, lse = _run(w, r, flags=flags)
     d = Device(w)
-    out0, lse0 = d.result()
+    out0, lse0 = d.result(flags=flags)
     assert np.array_equal(out, out0) and np.array_equal(lse, lse0)
