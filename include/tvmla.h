@@ -233,6 +233,38 @@ tvmla_status tvmla_verify_ragged(const void* q_nope, int64_t q_nope_stride_tok, 
                                  uint32_t flags, float fold_log2);
 
 /*
+ * For callers that cannot allocate: code under hipGraph capture that must
+ * not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation. The same call as tvmla_verify_ex, minus workspace and
+ * workspace_bytes: the split partials go to a scratch array the library
+ * owns in device memory, TVMLA_NOALLOC_SCRATCH_BYTES (256 MiB) per device,
+ * held from the library's load until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - Limit: calls whose workspace (tvmla_workspace_bytes' layout at the
+ *     split count the call runs: nsplit, or tvmla_effective_nsplit(...) with
+ *     TVMLA_FLAG_TUNE_NSPLIT) exceeds the scratch return TVMLA_E_WORKSPACE
+ *     and enqueue nothing. E.g. 16 draft tokens x 64 heads fit up to 120
+ *     splits of one request (the tuned 185k-context call runs 32).
+ *   - All calls on one device share that device's array; it keeps the last
+ *     call's partials, and nothing in it needs clearing between calls.
+ *     Calls that overlap on one device (different streams, or host threads
+ *     enqueueing concurrently) race on it: serialise them.
+ *   - The first call on a device looks the array's device address up (with
+ *     that device current) and caches it; `stream` must belong to the
+ *     current device (else TVMLA_E_VALUE).
+ * Other arguments, checks and results: as tvmla_verify_ex.
+ */
+#define TVMLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+tvmla_status tvmla_verify_noalloc(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                  const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                  const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                  const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                  const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                                  int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                                  int32_t dtype, void* out, float* lse, void* stream, int32_t algo,
+                                  int32_t min_chunk, uint32_t flags, float fold_log2);
+
+/*
  * The split step alone: the same arguments as tvmla_verify_ex without out,
  * lse and flags (nsplit is always used as given). It enqueues only the split
  * kernel, which leaves every non-empty split's partial result in the

@@ -37,7 +37,8 @@ STATUS = {
 # every symbol include/tvmla.h declares
 EXPORTS = ("tvmla_workspace_bytes", "tvmla_verify", "tvmla_verify_ex", "tvmla_verify_ragged", "tvmla_verify_partials",
            "tvmla_combine", "tvmla_defrag", "tvmla_tree_mask", "tvmla_status_str", "tvmla_version",
-           "tvmla_auto_algo", "tvmla_effective_nsplit", "tvmla_check_metadata")
+           "tvmla_auto_algo", "tvmla_effective_nsplit", "tvmla_check_metadata", "tvmla_verify_noalloc")
+NOALLOC_SCRATCH_BYTES = 256 << 20  # TVMLA_NOALLOC_SCRATCH_BYTES
 
 
 class TvmlaError(RuntimeError):
@@ -70,6 +71,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_verify.restype = ctypes.c_int
     lib.tvmla_verify_ex.argtypes = _VERIFY_ARGS + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_ex.restype = ctypes.c_int
+    lib.tvmla_verify_noalloc.argtypes = _VERIFY_ARGS[:21] + [_P, _I32, _I32, _U32, _F32]
+    lib.tvmla_verify_noalloc.restype = ctypes.c_int
     lib.tvmla_verify_ragged.argtypes = _VERIFY_ARGS[:13] + [_P] + _VERIFY_ARGS[13:] + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_ragged.restype = ctypes.c_int
     lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32, _F32]
@@ -203,6 +206,24 @@ def verify_plain(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc,
         batch, num_draft, H, float(sm_scale), nsplit, dt,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_ptr(stream))
+    _check(st)
+
+
+def verify_noalloc(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                   sm_scale: float, nsplit: int, out, lse, num_draft: int, algo: int = ALGO_AUTO,
+                   min_chunk: int = 0, flags: int = 0, fold_log2: float = FOLD_DEFAULT, stream=None) -> None:
+    """Enqueue tvmla_verify_noalloc: verify() without a workspace (the split
+    partials go to the library's per-device scratch array; calls on one
+    device must not overlap)."""
+    batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
+    _out_args(q_nope, out, lse)
+    st = load().tvmla_verify_noalloc(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0),
+        _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
+        batch, num_draft, H, float(sm_scale), nsplit, dt,
+        _ptr(out), _ptr(lse), _stream_ptr(stream), algo, min_chunk, flags, float(fold_log2))
     _check(st)
 
 

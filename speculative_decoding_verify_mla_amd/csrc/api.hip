@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 using namespace tvmla;
 
@@ -74,6 +75,37 @@ int32_t auto_bf16(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t n
   const int64_t rows = (int64_t)num_draft * num_heads;
   const int64_t wgs = (int64_t)batch * nsplit * ((rows + 127) / 128);
   return wgs >= 256 ? TVMLA_ALGO_ROWS : TVMLA_ALGO_MFMA;
+}
+
+// Library-owned scratch for tvmla_verify_noalloc: the split partials of
+// callers that cannot allocate a workspace. Each device the library runs on
+// holds its own copy until the process ends. In host code `noalloc_scratch`
+// names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever handed to a kernel.
+__device__ __align__(256) char noalloc_scratch[TVMLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// device's first call, then cached).
+tvmla_status noalloc_scratch_address(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TVMLA_E_LAUNCH;
+  // the kernels run on the stream's device; its scratch address is only
+  // known here for the current device
+  hipDevice_t sdev = dev;
+  if (stream != nullptr && (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev)) return TVMLA_E_VALUE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || p == nullptr) return TVMLA_E_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TVMLA_OK;
 }
 
 }  // namespace
@@ -289,6 +321,37 @@ tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t
                      kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                      nullptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse, workspace,
                      workspace_bytes, stream, TVMLA_ALGO_AUTO, 0, 0u, -1.f);
+}
+
+tvmla_status tvmla_verify_noalloc(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
+                                  const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
+                                  const void* kv_cache, int64_t kv_stride_row, const int32_t* kv_indptr,
+                                  const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                  const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
+                                  int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
+                                  int32_t dtype, void* out, float* lse, void* stream, int32_t algo,
+                                  int32_t min_chunk, uint32_t flags, float fold_log2) {
+  // every host check before the first HIP call, the scratch size included
+  if (flags & ~(uint32_t)TVMLA_FLAG_TUNE_NSPLIT) return TVMLA_E_VALUE;
+  if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return TVMLA_E_SHAPE;
+  const int32_t ns = (flags & TVMLA_FLAG_TUNE_NSPLIT) ? effective_nsplit(batch, num_draft, num_heads, nsplit) : nsplit;
+  if (workspace_layout(batch, num_draft, num_heads, ns).total > (size_t)TVMLA_NOALLOC_SCRATCH_BYTES)
+    return TVMLA_E_WORKSPACE;
+  SplitParams probe;
+  int32_t algo_checked = algo;
+  tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
+                            q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
+                            custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, ns, dtype, out, lse, true,
+                            reinterpret_cast<void*>(256), (size_t)TVMLA_NOALLOC_SCRATCH_BYTES, algo_checked,
+                            min_chunk, fold_log2, probe);
+  if (st != TVMLA_OK) return st;
+  void* scratch = nullptr;
+  st = noalloc_scratch_address(static_cast<hipStream_t>(stream), &scratch);
+  if (st != TVMLA_OK) return st;
+  return verify_impl(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok, q_rope_stride_head,
+                     kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                     nullptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, out, lse, scratch,
+                     (size_t)TVMLA_NOALLOC_SCRATCH_BYTES, stream, algo, min_chunk, flags, fold_log2);
 }
 
 tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,

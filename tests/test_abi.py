@@ -317,3 +317,18 @@ def test_tree_mask_null_pointer(lib, field):
 @pytest.mark.parametrize("kw", [dict(batch=0), dict(batch=65536), dict(T=0), dict(T=65)])
 def test_tree_mask_bad_shape(lib, kw):
     assert _tree_mask(lib, **kw) == 2
+
+
+def test_noalloc_host_checks(lib):
+    """tvmla_verify_noalloc rejects on the host, before any HIP call: a
+    workspace beyond its scratch, bad flags, a NULL pointer, a bad shape."""
+    f = lib.tvmla_verify_noalloc
+    good = [_FAKE, 64 * 512, 512, _FAKE, 64 * 64, 64, _FAKE, 576, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, 16, 64, 0.07,
+            64, binding.BF16, _FAKE, _FAKE, None, 0, 0, 0, -1.0]
+    # 1024 rows x 128 splits x 2 KB = 256 MiB, plus the lse region: one step past the scratch
+    assert _layout_bytes(1, 16, 64, 128) > binding.NOALLOC_SCRATCH_BYTES >= _layout_bytes(1, 16, 64, 127)
+    for idx, val, code in [(17, 128, 4), (24, 2, 8), (0, None, 1), (19, None, 1), (13, 0, 2), (17, 0, 2),
+                           (18, 5, 3), (16, 0.0, 8), (6, _FAKE + 2, 5)]:
+        a = list(good)
+        a[idx] = val
+        assert f(*a) == code, (idx, val)
