@@ -361,10 +361,16 @@ def main(argv=None):
                     help="defrag: time tvmla_defrag on the workload (a separate diagnostic line, not the "
                          "verify bench line) and the verify step before and after compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="run only the settle phase, the warm-up and the K timed steps of the bench call (no "
+                         "split-only, combine-only or exact-NSPLIT timings, graph replays, peaks or CPU baseline), "
+                         "so that a profiler run sees one dispatch shape per kernel")
     ap.add_argument("--build-probe", action="store_true",
                     help="compile the MFMA throughput probe (libtvmla_probe.so) and exit; no GPU needed")
     ap.add_argument("--report", action="store_true",
                     help="one diagnostic line per synthetic configuration instead of the bench line")
+    ap.add_argument("--report-workloads", default=",".join(REPORT_WORKLOADS),
+                    help="comma-separated configurations for --report")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the verify step, time a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM traffic counters)")
@@ -411,6 +417,8 @@ def main(argv=None):
         return bench_defrag(args, w, torch, binding)
     if args.op == "tree_mask":
         return bench_tree_mask(args, w, torch, binding)
+    if args.step_only:
+        return step_only(args, w, torch, binding)
     res = measure(args, w, args.workload, torch, binding)
     res["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu_baseline:
@@ -418,6 +426,47 @@ def main(argv=None):
         host_pool = w.host_pool(fill=0.0)
         res["cpu_baseline"] = cpu_baseline(w, host_pool)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+def step_only(args, w, torch, binding):
+    """The bench call alone (tuned split count), for profiler runs: settle,
+    warm-up, then K timed steps; prints us per call."""
+    dev = "cuda"
+    T, H, ns = w.num_draft, w.num_heads, w.spec.nsplit
+    pool = w.device_pool(dev, fill=0.0)
+    q_nope, q_rope = w.q_nope.to(dev), w.q_rope.to(dev)
+    kv_indptr, kv_indices = w.kv_indptr.to(dev), w.kv_indices.to(dev)
+    ocl, mask, mask_indptr = w.out_cache_loc.to(dev), w.custom_mask.to(dev), w.mask_indptr.to(dev)
+    out = torch.empty((w.batch * T, H, 512), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((w.batch * T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.workspace_bytes(w.batch, T, H, ns), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.verify(q_nope, q_rope, pool, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out, lse,
+                       ws, T, algo=args.algo, min_chunk=args.min_chunk, flags=binding.TUNE_NSPLIT, stream=stream)
+
+    t0 = time.perf_counter()
+    settle = 0
+    while time.perf_counter() - t0 < 0.15:
+        for _ in range(10):
+            step()
+        settle += 10
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"workload": args.workload, "us_per_call": round(ms * 1e3, 2), "settle_calls": settle,
+                      "warmup": args.warmup, "steps": args.steps,
+                      "nsplit_effective": binding.effective_nsplit(w.batch, T, H, ns)}), flush=True)
     return 0
 
 
@@ -462,12 +511,15 @@ def measure(args, w, name, torch, binding, graph=True):
             binding.verify(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale, ns, out,
                            lse, ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
 
+    # the two steps apart, launched exactly as the tuned call launches them
     def split_only():
         binding.verify_partials(q_nope, q_rope, kv, kv_indptr, kv_indices, ocl, mask, mask_indptr, w.sm_scale,
-                                ns_eff, ws, T, algo=args.algo, min_chunk=args.min_chunk, stream=stream)
+                                ns_eff, ws, T, algo=args.algo, min_chunk=args.min_chunk, flags=binding.TILE_CHUNKS,
+                                stream=stream)
 
     def combine_only():
-        binding.combine(ws, kv_indptr, w.batch, T, H, ns_eff, out, lse, min_chunk=args.min_chunk, stream=stream)
+        binding.combine(ws, kv_indptr, w.batch, T, H, ns_eff, out, lse, min_chunk=args.min_chunk,
+                        flags=binding.TILE_CHUNKS, stream=stream)
 
     def timed(fn, k):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -572,7 +624,7 @@ def report(args, torch, binding):
     model recorded)."""
     from workloads import gen
 
-    for name in REPORT_WORKLOADS:
+    for name in args.report_workloads.split(","):
         w = gen.build(name)
         r = measure(args, w, name, torch, binding)
         alg = algorithmic(w)

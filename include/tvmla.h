@@ -86,14 +86,28 @@ typedef enum {
  * TVMLA_FLAG_TUNE_NSPLIT: run tvmla_effective_nsplit(batch, num_draft,
  *   num_heads, nsplit) splits instead of exactly nsplit -- more splits when
  *   the grid would leave compute units idle, fewer when it would take more
- *   than one round of workgroups. Still a fixed function of the sizes, so a
- *   captured graph keeps its grid; the merged result equals the one at
- *   nsplit up to rounding (the log-sum-exp merge is exact in real
- *   arithmetic). Without it the call runs exactly the caller's nsplit, the
- *   fixed split count of "The Architecture of Capture Safety", section "The
- *   NSPLIT Calculation".
+ *   than one round of workgroups -- and round each split's chunk up to whole
+ *   64-key tiles: chunk = 64 * ceil(max(ceil(N_b / ns), min_chunk) / 64),
+ *   ns the effective count, so no split ends on a sliver of a tile (trailing
+ *   splits may then hold no keys; they return at once and are never read).
+ *   Still a fixed function of the sizes, so a captured graph keeps its grid;
+ *   the merged result equals the one at nsplit up to rounding (the
+ *   log-sum-exp merge is exact in real arithmetic). Without it the call runs
+ *   exactly the caller's nsplit with the pages' chunk, the fixed split count
+ *   of "The Architecture of Capture Safety", section "The NSPLIT
+ *   Calculation".
  */
 #define TVMLA_FLAG_TUNE_NSPLIT 1u
+/*
+ * TVMLA_FLAG_TILE_CHUNKS: round each split's chunk up to whole 64-key tiles
+ *   (as TVMLA_FLAG_TUNE_NSPLIT does) while keeping nsplit as given. Accepted
+ *   by every verify entry point, tvmla_verify_partials and tvmla_combine, so
+ *   the two separate steps can reproduce a tuned call's schedule exactly:
+ *   tvmla_verify_partials + tvmla_combine at tvmla_effective_nsplit(...)
+ *   splits with this flag launch what tvmla_verify_ex with
+ *   TVMLA_FLAG_TUNE_NSPLIT launches.
+ */
+#define TVMLA_FLAG_TILE_CHUNKS 2u
 
 /*
  * fold_log2 (tvmla_verify_ex, _ragged, _partials): TVMLA_ALGO_ROWS keeps
@@ -190,7 +204,8 @@ tvmla_status tvmla_verify(const void* q_nope, int64_t q_nope_stride_tok, int64_t
  *              longer splits (the launch is unchanged; surplus splits return
  *              at once), which cuts partial-result traffic; the result
  *              differs only by rounding.
- *   flags      0 or TVMLA_FLAG_TUNE_NSPLIT (other bits: TVMLA_E_VALUE)
+ *   flags      TVMLA_FLAG_TUNE_NSPLIT and/or TVMLA_FLAG_TILE_CHUNKS (other
+ *              bits: TVMLA_E_VALUE)
  *   fold_log2  the fold threshold described above (negative: default)
  */
 tvmla_status tvmla_verify_ex(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
@@ -265,13 +280,14 @@ tvmla_status tvmla_verify_noalloc(const void* q_nope, int64_t q_nope_stride_tok,
                                   int32_t min_chunk, uint32_t flags, float fold_log2);
 
 /*
- * The split step alone: the same arguments as tvmla_verify_ex without out,
- * lse and flags (nsplit is always used as given). It enqueues only the split
+ * The split step alone: the same arguments as tvmla_verify_ex without out
+ * and lse; nsplit is always used as given, so flags may only hold
+ * TVMLA_FLAG_TILE_CHUNKS (else TVMLA_E_VALUE). It enqueues only the split
  * kernel, which leaves every non-empty split's partial result in the
  * workspace (layout under tvmla_workspace_bytes); tvmla_combine with the same
- * kv_indptr, nsplit and min_chunk then produces exactly what tvmla_verify_ex
- * does at that split count. Callers that merge partials from several
- * sources, or that time the two steps apart, use the pair.
+ * kv_indptr, nsplit, min_chunk and flags then produces exactly what
+ * tvmla_verify_ex does at that split count. Callers that merge partials from
+ * several sources, or that time the two steps apart, use the pair.
  */
 tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok, int64_t q_nope_stride_head,
                                    const void* q_rope, int64_t q_rope_stride_tok, int64_t q_rope_stride_head,
@@ -280,7 +296,7 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
                                    const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                                    int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                                   int32_t algo, int32_t min_chunk, float fold_log2);
+                                   int32_t algo, int32_t min_chunk, uint32_t flags, float fold_log2);
 
 /*
  * The combine step alone: merge per-split partials laid out as in
@@ -290,14 +306,16 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
  *
  * If kv_indptr is non-NULL, split s of request b is read only when it holds
  * keys under the schedule above (N_b = kv_indptr[b+1]-kv_indptr[b]+num_draft,
- * chunk = max(ceil(N_b/nsplit), min_chunk)); other splits are never read.
+ * chunk = max(ceil(N_b/nsplit), min_chunk), rounded up to whole 64-key tiles
+ * with TVMLA_FLAG_TILE_CHUNKS, the only flag accepted); other splits are
+ * never read.
  * If kv_indptr is NULL every split is read and a split with lse = -inf
  * weighs nothing. A row whose splits are all -inf gets out = 0, lse = -inf.
  * workspace: as for tvmla_verify (read only here).
  */
 tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,
                            int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit,
-                           int32_t min_chunk, int32_t dtype, void* out, float* lse, void* stream);
+                           int32_t min_chunk, uint32_t flags, int32_t dtype, void* out, float* lse, void* stream);
 
 /*
  * KV defragmentation: copy every request's prefix rows into one contiguous

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libtvmla.so")
 BF16, FP32 = 0, 1
 ALGO_AUTO, ALGO_SCALAR, ALGO_MFMA, ALGO_ROWS = 0, 1, 2, 3
 TUNE_NSPLIT = 1  # TVMLA_FLAG_TUNE_NSPLIT
+TILE_CHUNKS = 2  # TVMLA_FLAG_TILE_CHUNKS
 FOLD_DEFAULT = -1.0  # fold_log2 < 0: the library's default threshold
 META_ARRAYS = {0: "none", 1: "kv_indptr", 2: "kv_indices", 3: "out_cache_loc", 4: "mask_indptr", 5: "qo_indptr"}
 D_LATENT, D_ROPE, D_KEY = 512, 64, 576
@@ -75,9 +76,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tvmla_verify_noalloc.restype = ctypes.c_int
     lib.tvmla_verify_ragged.argtypes = _VERIFY_ARGS[:13] + [_P] + _VERIFY_ARGS[13:] + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_ragged.restype = ctypes.c_int
-    lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32, _F32]
+    lib.tvmla_verify_partials.argtypes = _VERIFY_ARGS[:19] + _VERIFY_ARGS[21:] + [_I32, _I32, _U32, _F32]
     lib.tvmla_verify_partials.restype = ctypes.c_int
-    lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
+    lib.tvmla_combine.argtypes = [_P, _SZ, _P, _I32, _I32, _I32, _I32, _I32, _U32, _I32, _P, _P, _P]
     lib.tvmla_combine.restype = ctypes.c_int
     lib.tvmla_defrag.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I32, _I32, _P]
     lib.tvmla_defrag.restype = ctypes.c_int
@@ -257,7 +258,7 @@ def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc
 
 def verify_partials(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                     sm_scale: float, nsplit: int, workspace, num_draft: int, algo: int = ALGO_AUTO,
-                    min_chunk: int = 0, fold_log2: float = FOLD_DEFAULT, stream=None) -> None:
+                    min_chunk: int = 0, fold_log2: float = FOLD_DEFAULT, flags: int = 0, stream=None) -> None:
     """Enqueue tvmla_verify_partials: the split step only (partials land in workspace)."""
     batch, H, dt = _verify_args(q_nope, q_rope, kv_cache, num_draft)
     st = load().tvmla_verify_partials(
@@ -267,15 +268,15 @@ def verify_partials(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_l
         _ptr(kv_indptr), _ptr(kv_indices), _ptr(out_cache_loc), _ptr(custom_mask), _ptr(mask_indptr),
         batch, num_draft, H, float(sm_scale), nsplit, dt,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream_ptr(stream), algo, min_chunk, float(fold_log2))
+        _stream_ptr(stream), algo, min_chunk, flags, float(fold_log2))
     _check(st)
 
 
 def combine(workspace, kv_indptr, batch: int, num_draft: int, num_heads: int, nsplit: int, out, lse,
-            min_chunk: int = 0, stream=None) -> None:
+            min_chunk: int = 0, flags: int = 0, stream=None) -> None:
     """Enqueue tvmla_combine: merge the workspace's split partials into out/lse."""
     st = load().tvmla_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(kv_indptr),
-                              batch, num_draft, num_heads, nsplit, min_chunk, _dtype_code(out),
+                              batch, num_draft, num_heads, nsplit, min_chunk, flags, _dtype_code(out),
                               _ptr(out), _ptr(lse), _stream_ptr(stream))
     _check(st)
 

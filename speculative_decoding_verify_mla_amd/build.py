@@ -57,10 +57,15 @@ def _run(cmd, verbose):
     return out
 
 
+RESOURCE_REPORT = os.path.join(BUILD, "resource_usage.txt")
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libtvmla.so. Returns its path."""
+    """Compile every HIP source for gfx950 and link libtvmla.so. Returns its
+    path. The compiler's per-kernel resource report (registers, LDS, scratch)
+    is kept in _build/resource_usage.txt (printed with resource_usage=True)."""
     os.makedirs(BUILD, exist_ok=True)
-    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    extra = ["-Rpass-analysis=kernel-resource-usage"]
 
     def one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
@@ -70,9 +75,11 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         results = list(ex.map(one, SOURCES))
+    report = "\n".join(line for _, out in results for line in out.splitlines() if "remark:" in line)
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write(report + "\n")
     if resource_usage:
-        for _, out in results:
-            print(out)
+        print(report)
     objs = [o for o, _ in results]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)

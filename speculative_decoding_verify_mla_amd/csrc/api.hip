@@ -21,6 +21,14 @@ namespace {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// Keys per tile of the MFMA split kernels: with TVMLA_FLAG_TILE_CHUNKS (or
+// TVMLA_FLAG_TUNE_NSPLIT, which implies it) each split's chunk is rounded up
+// to a multiple of it, so no split ends on a sliver of a tile.
+constexpr int32_t kTileKeys = 64;
+int32_t chunk_align(uint32_t flags) {
+  return (flags & (TVMLA_FLAG_TUNE_NSPLIT | TVMLA_FLAG_TILE_CHUNKS)) ? kTileKeys : 1;
+}
+
 tvmla_status check_shape(int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit) {
   if (batch < 1 || batch > 65535) return TVMLA_E_SHAPE;
   if (num_draft < 1 || num_draft > TVMLA_MAX_DRAFT) return TVMLA_E_SHAPE;
@@ -205,6 +213,7 @@ static tvmla_status prepare(const void* q_nope, int64_t q_nope_stride_tok, int64
   p.num_heads = num_heads;
   p.nsplit = nsplit;
   p.min_chunk = min_chunk;
+  p.chunk_align = 1;
   p.sm_scale = sm_scale;
   char* ws = static_cast<char*>(workspace);
   p.o_part = reinterpret_cast<float*>(ws + wl.o_off);
@@ -232,7 +241,7 @@ static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, i
                                 int32_t batch, int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                 int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream, int32_t algo, int32_t min_chunk, uint32_t flags, float fold_log2) {
-  if (flags & ~(uint32_t)TVMLA_FLAG_TUNE_NSPLIT) return TVMLA_E_VALUE;
+  if (flags & ~(uint32_t)(TVMLA_FLAG_TUNE_NSPLIT | TVMLA_FLAG_TILE_CHUNKS)) return TVMLA_E_VALUE;
   SplitParams p;
   if (flags & TVMLA_FLAG_TUNE_NSPLIT) nsplit = effective_nsplit(batch, num_draft, num_heads, nsplit);
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
@@ -241,6 +250,7 @@ static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, i
                             true, workspace, workspace_bytes, algo, min_chunk, fold_log2, p);
   if (st != TVMLA_OK) return st;
   p.qo_indptr = qo_indptr;
+  p.chunk_align = chunk_align(flags);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_split(p, algo, dtype, s) != hipSuccess) return TVMLA_E_LAUNCH;
 
@@ -253,6 +263,7 @@ static tvmla_status verify_impl(const void* q_nope, int64_t q_nope_stride_tok, i
   c.num_heads = num_heads;
   c.nsplit = nsplit;
   c.min_chunk = min_chunk;
+  c.chunk_align = p.chunk_align;
   c.qo_indptr = qo_indptr;
   c.out = out;
   c.lse = lse;
@@ -298,13 +309,15 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
                                    const uint8_t* custom_mask, const int32_t* mask_indptr, int32_t batch,
                                    int32_t num_draft, int32_t num_heads, float sm_scale, int32_t nsplit,
                                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                                   int32_t algo, int32_t min_chunk, float fold_log2) {
+                                   int32_t algo, int32_t min_chunk, uint32_t flags, float fold_log2) {
+  if (flags & ~(uint32_t)TVMLA_FLAG_TILE_CHUNKS) return TVMLA_E_VALUE;
   SplitParams p;
   tvmla_status st = prepare(q_nope, q_nope_stride_tok, q_nope_stride_head, q_rope, q_rope_stride_tok,
                             q_rope_stride_head, kv_cache, kv_stride_row, kv_indptr, kv_indices, out_cache_loc,
                             custom_mask, mask_indptr, batch, num_draft, num_heads, sm_scale, nsplit, dtype, nullptr,
                             nullptr, false, workspace, workspace_bytes, algo, min_chunk, fold_log2, p);
   if (st != TVMLA_OK) return st;
+  p.chunk_align = chunk_align(flags);
   if (launch_split(p, algo, dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return TVMLA_E_LAUNCH;
   return TVMLA_OK;
 }
@@ -332,7 +345,7 @@ tvmla_status tvmla_verify_noalloc(const void* q_nope, int64_t q_nope_stride_tok,
                                   int32_t dtype, void* out, float* lse, void* stream, int32_t algo,
                                   int32_t min_chunk, uint32_t flags, float fold_log2) {
   // every host check before the first HIP call, the scratch size included
-  if (flags & ~(uint32_t)TVMLA_FLAG_TUNE_NSPLIT) return TVMLA_E_VALUE;
+  if (flags & ~(uint32_t)(TVMLA_FLAG_TUNE_NSPLIT | TVMLA_FLAG_TILE_CHUNKS)) return TVMLA_E_VALUE;
   if (check_shape(batch, num_draft, num_heads, nsplit) != TVMLA_OK) return TVMLA_E_SHAPE;
   const int32_t ns = (flags & TVMLA_FLAG_TUNE_NSPLIT) ? effective_nsplit(batch, num_draft, num_heads, nsplit) : nsplit;
   if (workspace_layout(batch, num_draft, num_heads, ns).total > (size_t)TVMLA_NOALLOC_SCRATCH_BYTES)
@@ -356,7 +369,8 @@ tvmla_status tvmla_verify_noalloc(const void* q_nope, int64_t q_nope_stride_tok,
 
 tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const int32_t* kv_indptr,
                            int32_t batch, int32_t num_draft, int32_t num_heads, int32_t nsplit,
-                           int32_t min_chunk, int32_t dtype, void* out, float* lse, void* stream) {
+                           int32_t min_chunk, uint32_t flags, int32_t dtype, void* out, float* lse, void* stream) {
+  if (flags & ~(uint32_t)TVMLA_FLAG_TILE_CHUNKS) return TVMLA_E_VALUE;
   if (dtype != TVMLA_BF16 && dtype != TVMLA_FP32) return TVMLA_E_DTYPE;
   if (!out || !lse) return TVMLA_E_NULLPTR;
   if (!workspace) return TVMLA_E_WORKSPACE;
@@ -376,6 +390,7 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
   c.num_heads = num_heads;
   c.nsplit = nsplit;
   c.min_chunk = min_chunk;
+  c.chunk_align = chunk_align(flags);
   c.qo_indptr = nullptr;
   c.out = out;
   c.lse = lse;

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
   int ns = c.nsplit;
   if (c.kv_indptr != nullptr) {
     const int n = c.kv_indptr[b + 1] - c.kv_indptr[b] + Tb;
-    ns = active_splits(n, c.nsplit, c.min_chunk);
+    ns = active_splits(n, c.nsplit, c.min_chunk, c.chunk_align);
   }
   const size_t base = (size_t)b * c.nsplit * R + r;  // partial row of split 0
   const int nu = ns > wr ? (ns - wr + W - 1) / W : 0;  // this wavefront's splits
@@ -213,10 +213,10 @@ __global__ __launch_bounds__(W == 16 ? 1024 : 256) void combine_kernel(CombinePa
   if (kBf16) {
     uint16_t* dst = static_cast<uint16_t*>(c.out) + orow * kDLatent + 8 * lane;
     uint4 u;
-    u.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
-    u.w = (uint32_t)f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
+    u.x = pack_bf16x2(acc[0], acc[1]);
+    u.y = pack_bf16x2(acc[2], acc[3]);
+    u.z = pack_bf16x2(acc[4], acc[5]);
+    u.w = pack_bf16x2(acc[6], acc[7]);
     *reinterpret_cast<uint4*>(dst) = u;
   } else {
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(c.out) + orow * kDLatent + 8 * lane);

@@ -232,7 +232,7 @@ void split_mfma_kernel(SplitParams p, int groups, int pairs) {
   const int P = p.kv_indptr[b + 1] - ip0;
   const int N = P + Tb;
   int start, end;
-  split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
+  split_bounds(N, p.nsplit, p.min_chunk, p.chunk_align, s, start, end);
   if (start >= end) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

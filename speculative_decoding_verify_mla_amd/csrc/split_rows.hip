@@ -214,6 +214,10 @@ __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -280,7 +284,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const int P = p.kv_indptr[b + 1] - ip0;
   const int N = P + Tb;
   int start, end;
-  split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
+  split_bounds(N, p.nsplit, p.min_chunk, p.chunk_align, s, start, end);
   if (start >= end) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -323,9 +327,13 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   float m_slot = 0.f;       // the reference of the slot's folded sum
   bool folded = false;      // the partial-result slot holds a folded accumulator (wavefront-uniform)
   const bf16x8_t zero8 = {};
-  const size_t prow = ((size_t)b * p.nsplit + s) * Rw + r;  // partial-result row (valid when r < R)
-  float* fold_dst = p.o_part + prow * kDLatent + 4 * hf;
-  const float* slot0 = p.o_part + (prow - col) * kDLatent;  // slot of the wavefront's row 0
+  // Partial-result row (valid when r < R). A workspace that fits in memory
+  // has fewer than 2^32 rows of 2 KB. The 64-bit slot addresses are formed
+  // where they are used (fold path, epilogue) from an opaque copy of it, not
+  // kept in registers across the tile loop (which would spill them to
+  // scratch, and a kernel that uses scratch pays several microseconds more
+  // per launch).
+  const uint32_t prow = (uint32_t)(((size_t)b * p.nsplit + s) * Rw + r);
   const int rows_valid = min(32, R - (g * kRowsWG + 32 * wave));
 
   const float scale2 = p.sm_scale * kLog2e;
@@ -588,6 +596,9 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     auto fold = [&]() {
       // slot = O + slot * 2^(m_slot - m_ref), against m_ref (a row with
       // nothing accumulated at the last fold has m_slot = -inf and a zero slot)
+      const uint32_t pr = opaque(prow);
+      float* fold_dst = p.o_part + (size_t)pr * kDLatent + 4 * hf;
+      const float* slot0 = p.o_part + (size_t)(pr - col) * kDLatent;  // slot of the wavefront's row 0
       const float beta = m_slot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_slot - m_ref);
       TVMLA_O_DRAIN(o);
       if (folded) add_slots(o, slot0, rows_valid, beta, ln);
@@ -643,16 +654,17 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   TVMLA_O_DRAIN(o);
 
   // The folded part (against m_slot) joins the accumulator (against m_ref).
+  const uint32_t pr = opaque(prow);
   const float beta = folded && m_slot != -INFINITY ? __builtin_amdgcn_exp2f(m_slot - m_ref) : 0.f;
   if (folded) {
-    add_slots(o, slot0, rows_valid, beta, lane);
+    add_slots(o, p.o_part + (size_t)(pr - col) * kDLatent, rows_valid, beta, lane);
     TVMLA_O_DRAIN(o);
   }
   const float lsum = l_fold * beta + l_part;
   const float l = lsum + __shfl_xor(lsum, 32, 64);
   if (r >= R) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* dst = partial_bf16(p.o_part, prow) + 4 * hf;  // the row's output as bf16 (the slot's first 1 KB)
+  uint16_t* dst = partial_bf16(p.o_part, pr) + 4 * hf;  // the row's output as bf16 (the slot's first 1 KB)
 #pragma unroll
   for (int db = 0; db < 16; ++db)
 #pragma unroll
@@ -660,7 +672,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       *reinterpret_cast<uint2*>(dst + 32 * db + 8 * jg) =
           pack_bf16x4(o[db][4 * jg + 0] * inv, o[db][4 * jg + 1] * inv, o[db][4 * jg + 2] * inv,
                       o[db][4 * jg + 3] * inv);
-  if (hf == 0) p.lse_part[prow] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+  if (hf == 0) p.lse_part[pr] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

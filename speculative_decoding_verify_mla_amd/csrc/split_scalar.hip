@@ -36,10 +36,10 @@ struct Elem<uint16_t> {  // bf16 bits
   __device__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
   __device__ static void store8(uint16_t* p, const float* v) {
     uint4 u;
-    u.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
-    u.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = u;
   }
 };
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(SplitParams p) {
   const int P = p.kv_indptr[b + 1] - ip0;
   const int N = P + Tb;
   int start, end;
-  split_bounds(N, p.nsplit, p.min_chunk, s, start, end);
+  split_bounds(N, p.nsplit, p.min_chunk, p.chunk_align, s, start, end);
   if (start >= end) return;  // empty split: nothing to write, the combine skips it
 
   const int i = r / p.num_heads;

@@ -27,6 +27,7 @@ struct SplitParams {
   const uint8_t* mask;
   const int32_t* mask_indptr;
   int32_t batch, num_draft, num_heads, nsplit, min_chunk;
+  int32_t chunk_align;  // chunks rounded up to a multiple of this (1: the pages' rule exactly)
   float sm_scale;
   float* o_part;    // [batch][nsplit][num_draft * num_heads][512]
   float* lse_part;  // [batch][nsplit][num_draft * num_heads]
@@ -39,6 +40,7 @@ struct CombineParams {
   const float* lse_part;
   const int32_t* kv_indptr;  // may be null: read every split
   int32_t batch, num_draft, num_heads, nsplit, min_chunk;
+  int32_t chunk_align;  // as SplitParams::chunk_align
   const int64_t* qo_indptr;  // null: num_draft tokens per request; else per-request token ranges
   void* out;
   float* lse;
@@ -79,11 +81,20 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_draft, int64_
   return w;
 }
 
-// Key range [start, end) of split s of a request with n keys: chunk =
-// max(ceil(n / nsplit), min_chunk), split s starts at s * chunk.
-__host__ __device__ inline void split_bounds(int n, int nsplit, int min_chunk, int s, int& start, int& end) {
-  int chunk = (n + nsplit - 1) / nsplit;
+// Keys per split of a request with n keys: max(ceil(n / nsplit),
+// min_chunk) rounded up to a multiple of align (align 1 and min_chunk 0
+// give the pages' ceil(n / nsplit)).
+__host__ __device__ inline int64_t split_chunk(int n, int nsplit, int min_chunk, int align) {
+  int64_t chunk = ((int64_t)n + nsplit - 1) / nsplit;
   if (chunk < min_chunk) chunk = min_chunk;
+  return (chunk + align - 1) / align * align;
+}
+
+// Key range [start, end) of split s of a request with n keys: split s
+// starts at s * split_chunk(...).
+__host__ __device__ inline void split_bounds(int n, int nsplit, int min_chunk, int align, int s, int& start,
+                                             int& end) {
+  const int64_t chunk = split_chunk(n, nsplit, min_chunk, align);
   const int64_t st = (int64_t)s * chunk;
   start = st < n ? (int)st : n;
   const int64_t en = st + chunk;
@@ -91,12 +102,11 @@ __host__ __device__ inline void split_bounds(int n, int nsplit, int min_chunk, i
 }
 
 // Number of leading splits that hold keys under split_bounds.
-__host__ __device__ inline int active_splits(int n, int nsplit, int min_chunk) {
+__host__ __device__ inline int active_splits(int n, int nsplit, int min_chunk, int align) {
   if (n <= 0) return 0;
-  int chunk = (n + nsplit - 1) / nsplit;
-  if (chunk < min_chunk) chunk = min_chunk;
-  const int a = (n + chunk - 1) / chunk;
-  return a < nsplit ? a : nsplit;
+  const int64_t chunk = split_chunk(n, nsplit, min_chunk, align);
+  const int64_t a = ((int64_t)n + chunk - 1) / chunk;
+  return a < nsplit ? (int)a : nsplit;
 }
 
 // Draft tokens of request b and the index of its first one: num_draft and
@@ -142,12 +152,12 @@ __device__ inline int request_of_rank(const SplitParams& p, int rank) {
   return __builtin_ctzll(__ballot(lane < p.batch && above == rank));
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 with round to nearest even (a NaN stays a NaN): the
+// hardware conversion, v_cvt_pk_bf16_f32, two values per instruction.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -155,8 +165,8 @@ __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32
 // Four fp32 values as bf16 (round to nearest even), packed into 8 bytes.
 __device__ inline uint2 pack_bf16x4(float a, float b, float c, float d) {
   uint2 u;
-  u.x = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
-  u.y = (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16);
+  u.x = pack_bf16x2(a, b);
+  u.y = pack_bf16x2(c, d);
   return u;
 }
 

@@ -433,15 +433,21 @@ def test_graph_capture_replay():
             assert np.array_equal(go, eo) and np.array_equal(gl, el)
 
 
+def _tuned_chunk(n, ns):
+    """Keys per split of the tuned call: ceil(n / ns) rounded up to whole 64-key tiles."""
+    return -(-(-(-n // ns)) // 64) * 64
+
+
 @pytest.mark.parametrize("name,ns,eff_expected", [
     ("ragged_h8", 7, 112),   # 3 requests x 40 rows: 21 workgroups, raised to 336
     ("groups_h64", 32, 16),  # 2 requests x 8 row groups: 512 workgroups, lowered to one round of 256
     ("groups4_h64", 64, 16),  # 4 requests x 8 row groups: 2048 workgroups, halved to 512 (two rounds)
 ])
 def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
-    """With TVMLA_FLAG_TUNE_NSPLIT the call runs the effective split count;
-    it is bit-identical to split + combine at that count, and matches the
-    oracle."""
+    """With TVMLA_FLAG_TUNE_NSPLIT the call runs the effective split count
+    with chunks rounded up to whole 64-key tiles; it matches the oracle and
+    is bit-identical to the split step and the combine at that count with
+    TVMLA_FLAG_TILE_CHUNKS."""
     spec = SMALL[name] if name in SMALL else gen.small(name, 4, [40, 300, 0, 129], 16, 64, seed=19)
     w = gen.build(spec)
     eff = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, ns)
@@ -452,22 +458,57 @@ def test_effective_nsplit_matches_explicit(name, ns, eff_expected):
         o1, l1 = d.result(algo=algo, flags=binding.TUNE_NSPLIT)
         compare(w, o1, l1, ref_out, ref_lse, f"{name}/nsplit{ns}->{eff}/algo{algo}")
         binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc,
-                                d.custom_mask, d.mask_indptr, w.sm_scale, eff, d.ws, w.num_draft, algo=algo)
-        binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, eff, d.out, d.lse)
+                                d.custom_mask, d.mask_indptr, w.sm_scale, eff, d.ws, w.num_draft, algo=algo,
+                                flags=binding.TILE_CHUNKS)
+        binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, eff, d.out, d.lse,
+                        flags=binding.TILE_CHUNKS)
         torch.cuda.synchronize()
         o2 = d.out.float().cpu().numpy().astype(np.float64)
         l2 = d.lse.cpu().numpy().astype(np.float64)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("flags", [0, binding.TUNE_NSPLIT])
-def test_partials_then_combine_equals_verify(flags):
+@pytest.mark.parametrize("algo", [ROWS, MFMA, SCALAR])
+def test_tile_chunks_flag(algo):
+    """TVMLA_FLAG_TILE_CHUNKS at the caller's split count (no tuning):
+    matches the oracle and the split step + combine with the same flag."""
+    w = gen.build(SMALL["ragged_h8"])
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w, nsplit=7)
+    o1, l1 = d.result(algo=algo, flags=binding.TILE_CHUNKS)
+    compare(w, o1, l1, ref_out, ref_lse, f"ragged_h8/tile_chunks/algo{algo}")
+    binding.verify_partials(d.q_nope, d.q_rope, d.pool, d.kv_indptr, d.kv_indices, d.out_cache_loc, d.custom_mask,
+                            d.mask_indptr, w.sm_scale, 7, d.ws, w.num_draft, algo=algo, flags=binding.TILE_CHUNKS)
+    binding.combine(d.ws, d.kv_indptr, w.batch, w.num_draft, w.num_heads, 7, d.out, d.lse, flags=binding.TILE_CHUNKS)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, d.out.float().cpu().numpy().astype(np.float64))
+    assert np.array_equal(l1, d.lse.cpu().numpy().astype(np.float64))
+
+
+def test_tuned_call_writes_whole_tile_splits():
+    """p4096 (4,112 keys) tuned to 32 splits: chunks of 192 keys (129 rounded
+    up to three 64-key tiles), so splits 0..21 hold keys and 22..31 are empty
+    and never written."""
+    w = gen.build("p4096")
+    d = Device(w)
+    eff = binding.effective_nsplit(1, 16, 64, 64)
+    assert eff == 32 and _tuned_chunk(4112, eff) == 192
+    d.ws.fill_(float("nan"))
+    d.run(flags=binding.TUNE_NSPLIT)
+    torch.cuda.synchronize()
+    _, l_ws = binding.workspace_views(d.ws, 1, 16, 64, eff, binding.BF16)
+    l_ws = l_ws.cpu().numpy()
+    assert np.isfinite(l_ws[0, :22]).all()
+    assert np.isnan(l_ws[0, 22:]).all()
+
+
+def test_partials_then_combine_equals_verify():
     w = gen.build(SMALL["groups_h64"])
     d = Device(w)
-    # the full call runs exactly nsplit splits, or the effective count when tuned; the two steps take it as given
-    ns = binding.effective_nsplit(w.batch, w.num_draft, w.num_heads, d.nsplit) if flags else d.nsplit
+    # the full call runs exactly nsplit splits; the two steps take it as given
+    ns = d.nsplit
     for algo in (ROWS, MFMA, SCALAR):
-        o1, l1 = d.result(algo=algo, flags=flags)
+        o1, l1 = d.result(algo=algo)
         d.out.fill_(float("nan"))
         d.lse.fill_(float("nan"))
         d.ws.fill_(float("nan"))
