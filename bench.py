@@ -104,7 +104,7 @@ def graph_timing(torch, call_on, replays=GRAPH_REPLAYS):
     return res
 
 
-PROBE_SRC = os.path.join(ROOT, "bench_mfma_probe.hip")
+PROBE_SRC = os.path.join(ROOT, "bench_probes.hip")
 PROBE_LIB = os.path.join(ROOT, "libtvmla_probe.so")
 
 
@@ -162,6 +162,57 @@ def measured_peaks(torch):
     ms = e0.elapsed_time(e1) / 5
     out["mfma_bf16_TFLOPs"] = round(probe.tvmla_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12, 1)
     return out
+
+
+def read_ceilings(torch, pool, kv_indices, kv_bytes):
+    """What this GPU sustains, cold (L2 and MALL flushed before each of 10
+    launches, median), for the bytes the verify call must read: a plain
+    streaming read of kv_bytes (the pool's first rows) and a gather of
+    exactly the workload's prefix rows through its kv_indices (the verify
+    path's access pattern without its arithmetic). Both from
+    bench_probes.hip; None if the probe library is not built."""
+    import ctypes
+
+    import numpy as np
+
+    if not os.path.exists(PROBE_LIB):
+        return None
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.tvmla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p]
+    probe.tvmla_probe_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    row_bytes = pool.stride(0) * pool.element_size()
+    nrows = int(kv_indices.numel())
+    gather_bytes = nrows * 576 * pool.element_size()
+    stream_bytes = min(kv_bytes, pool.numel() * pool.element_size()) // 16 * 16
+
+    def cold(launch):
+        for _ in range(3):
+            assert launch() == 0
+        ts = []
+        for i in range(10):
+            flush.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    t_stream = cold(lambda: probe.tvmla_probe_stream_read(pool.data_ptr(), stream_bytes, sink.data_ptr(), 2048,
+                                                          stream.cuda_stream))
+    # rows of 576 entries at the pool's row stride (1152 bytes for a bf16 pool of 576-wide rows)
+    t_gather = cold(lambda: probe.tvmla_probe_gather_rows(pool.data_ptr(), row_bytes, kv_indices.data_ptr(), nrows,
+                                                          sink.data_ptr(), 1024, stream.cuda_stream))
+    del flush
+    return {"stream_read_us": round(t_stream, 2), "stream_read_GBps": round(stream_bytes / (t_stream * 1e-6) / 1e9, 1),
+            "gather_rows_us": round(t_gather, 2), "gather_rows_GBps": round(gather_bytes / (t_gather * 1e-6) / 1e9, 1),
+            "bytes": stream_bytes, "rows": nrows, "row_bytes": int(row_bytes), "cache": "cold (1 GiB flushed)"}
 
 
 def profiled_traffic(kernel):
@@ -557,6 +608,7 @@ def measure(args, w, name, torch, binding, graph=True):
           f"{ms_combine * 1e3:.1f} us; tvmla_verify at nsplit {ns}: {ms_exact * 1e3:.1f} us", file=sys.stderr,
           flush=True)
     graph_us = graph_timing(torch, step_on) if graph else None
+    ceilings = read_ceilings(torch, pool, kv_indices, algorithmic(w)["kv_bytes"]) if graph else None
 
     alg = algorithmic(w)
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
@@ -611,6 +663,8 @@ def measure(args, w, name, torch, binding, graph=True):
     }
     if graph_us is not None:
         res["graph_us"] = graph_us
+    if ceilings is not None:
+        res["read_ceilings"] = ceilings
     del pool, kv, ws
     return res
 
@@ -641,7 +695,7 @@ def report(args, torch, binding):
             "roofline_frac": round(max(t_hbm, t_cmp) / t, 4),
             "t_hbm_us": round(t_hbm * 1e6, 2), "t_compute_us": round(t_cmp * 1e6, 2),
             "kernels_us": r["kernels_us"], "split_roofline": r["roofline"],
-            "nsplit_exact_call": r["nsplit_exact_call"],
+            "nsplit_exact_call": r["nsplit_exact_call"], "read_ceilings": r.get("read_ceilings"),
             "config": r["config"],
         }
         if not args.no_cpu_baseline:
