@@ -465,39 +465,64 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         for (int j = 0; j < 16; ++j) sm[h][j] = ((v >> (8 * (j >> 2) + (j & 3))) & 1u) ? sm[h][j] : -INFINITY;
       }
     };
-    // the block's maximum in five pieces (scores 0..4, 5..8, 9..12, 13..15,
-    // then the lane-half swap)
+    // The side work between MFMAs is issued in order with them: an
+    // instruction that waits on the one before it (an exp on its fma, an add
+    // on its exp) holds back the next MFMA as well. So the block maximum is
+    // a tree of independent v_max3 (two per gap) and each probability is
+    // three stages one gap apart.
+    //
+    // The block's maximum in six pieces: three gaps of two independent
+    // maxima of three scores, the maximum of those, then the lane-half swap.
+    float mx[6];
     auto max_part = [&](int h, int part) {
       if (part == 0) {
-        tmx[h] = max3(sm[h][0], sm[h][1], sm[h][2]);
-        tmx[h] = max3(tmx[h], sm[h][3], sm[h][4]);
-      } else if (part < 4) {
-        const int j = 4 * part + 1;
-        tmx[h] = max3(tmx[h], sm[h][j], sm[h][j + 1]);
-        tmx[h] = max3(tmx[h], sm[h][j + 2], sm[h][min(j + 3, 15)]);
+        mx[0] = max3(sm[h][0], sm[h][1], sm[h][2]);
+        mx[1] = max3(sm[h][3], sm[h][4], sm[h][5]);
+      } else if (part == 1) {
+        mx[2] = max3(sm[h][6], sm[h][7], sm[h][8]);
+        mx[3] = max3(sm[h][9], sm[h][10], sm[h][11]);
+      } else if (part == 2) {
+        mx[4] = max3(sm[h][12], sm[h][13], sm[h][14]);
+        mx[5] = max3(mx[0], mx[1], sm[h][15]);
+      } else if (part == 3) {
+        tmx[h] = max3(mx[2], mx[3], mx[4]);
+      } else if (part == 4) {
+        tmx[h] = max3(tmx[h], mx[5], mx[5]);
       } else {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx[h]), __float_as_uint(tmx[h]), false, false);
         tmx[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
       }
     };
-    // probability j of block h against mu = -m_ref (0 while m_ref = -inf);
-    // odd j also packs the pair into the P^T operand
+    constexpr int kMaxParts = 6;
+    // Probability j of block h against mu = -m_ref (0 while m_ref = -inf):
+    // F (the fma into pt[j]), E (exp2 in place), S (the running sum, and for
+    // odd j the pair packed into the P^T operand). prob_stage(h, k, mu) is
+    // gap k of the pipeline: S(k-2), E(k-1), F(k); gaps 0..17 cover j =
+    // 0..15, each stage one gap after the one it needs. The sum runs over
+    // j = 0..15 in order as before.
     float pt[16];
-    auto prob1 = [&](int h, int j, float mu) {
-      pt[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[h][j], scale2, mu));
+    auto prob_f = [&](int h, int j, float mu) { pt[j] = __builtin_fmaf(sm[h][j], scale2, mu); };
+    auto prob_e = [&](int j) { pt[j] = __builtin_amdgcn_exp2f(pt[j]); };
+    auto prob_s = [&](int h, int j) {
       psum[h] = j == 0 ? pt[j] : psum[h] + pt[j];
       if (j & 1) {
         pf[2 * h + (j >> 3)][(j & 7) - 1] = (__bf16)pt[j - 1];
         pf[2 * h + (j >> 3)][j & 7] = (__bf16)pt[j];
       }
     };
+    auto prob_stage = [&](int h, int k, float mu) {
+      if (k >= 2 && k < 18) prob_s(h, k - 2);
+      if (k >= 1 && k < 17) prob_e(k - 1);
+      if (k < 16) prob_f(h, k, mu);
+    };
+    constexpr int kProbGaps = 18;
     auto probs_block = [&](int h, float mu) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) prob1(h, j, mu);
+      for (int k = 0; k < kProbGaps; ++k) prob_stage(h, k, mu);
     };
     auto max_block = [&](int h) {
 #pragma unroll
-      for (int part = 0; part < 5; ++part) max_part(h, part);
+      for (int part = 0; part < kMaxParts; ++part) max_part(h, part);
     };
     const float mu0 = m_ref == -INFINITY ? 0.f : -m_ref;
 
@@ -575,12 +600,14 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         for (int j = 0; j < 16; ++j) sm[0][j] = sacc[0][j];
         mask_block(0);
       }
-      if constexpr (i >= 1 && i <= 5) max_part(0, i - 1);
-      if constexpr (i >= 6 && i < 22) prob1(0, i - 6, mu0);
+      if constexpr (i >= 1 && i <= kMaxParts) max_part(0, i - 1);
+      constexpr int k0 = i - (kMaxParts + 1);  // gap of block 0's probability pipeline
+      if constexpr (k0 >= 0 && k0 < kProbGaps) prob_stage(0, k0, mu0);
+      static_assert(kQSteps + 2 + kMaxParts + kProbGaps <= kSSteps, "block 0's softmax must fit under block 1's MFMAs");
       // Keep them here: the reference decision below recomputes them when
       // the reference moves, and the compiler would otherwise sink them into
       // the other branch, after the last score MFMA.
-      if constexpr (i == 21) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
+      if constexpr (k0 == kProbGaps - 1) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
       __builtin_amdgcn_sched_barrier(0);
     });
     stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
@@ -597,7 +624,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       // slot = O + slot * 2^(m_slot - m_ref), against m_ref (a row with
       // nothing accumulated at the last fold has m_slot = -inf and a zero slot)
       const uint32_t pr = opaque(prow);
-      float* fold_dst = p.o_part + (size_t)pr * kDLatent + 4 * hf;
+      float* fold_dst = p.o_part + (size_t)pr * kDLatent + 4 * opaque(hf);
       const float* slot0 = p.o_part + (size_t)(pr - col) * kDLatent;  // slot of the wavefront's row 0
       const float beta = m_slot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_slot - m_ref);
       TVMLA_O_DRAIN(o);
@@ -638,7 +665,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     static_for<0, kVRing>([&](auto x_) { vread(x_); });
     pv_steps(Int<0>{}, Int<32>{}, [&](auto i_) {
       constexpr int i = decltype(i_)::value;
-      if constexpr (i >= 1 && i < 17) prob1(1, i - 1, mu1);
+      if constexpr (i >= 1 && i < 1 + kProbGaps) prob_stage(1, i - 1, mu1);
     });
     l_part += psum[0] + psum[1];
     pv_steps(Int<32>{}, Int<64>{}, [](auto) {});
@@ -664,7 +691,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const float l = lsum + __shfl_xor(lsum, 32, 64);
   if (r >= R) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* dst = partial_bf16(p.o_part, pr) + 4 * hf;  // the row's output as bf16 (the slot's first 1 KB)
+  uint16_t* dst = partial_bf16(p.o_part, pr) + 4 * opaque(hf);  // the row's output as bf16 (the slot's first 1 KB)
 #pragma unroll
   for (int db = 0; db < 16; ++db)
 #pragma unroll
