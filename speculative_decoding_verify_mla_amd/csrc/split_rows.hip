@@ -9,11 +9,13 @@
 // section "The Design Reasoning", variants 2 and 3: read the shared latent
 // once, use it for many heads).
 //
-// LDS tile format, staging and value reads are those of the 64-row kernel:
-// a 64-key tile is a latent region (64 keys x 1024 bytes, the 16-byte pieces
-// of a key XOR-swizzled by a function of the key) and a rope region (64 keys
-// x 128 bytes), filled by direct global->LDS loads one tile ahead into a
-// second buffer.
+// LDS tile format: a 64-key tile is 8 groups of 8 keys. A key's cache row
+// is 9 chunks of 128 bytes (8 latent, 1 rope; one cache line each), and
+// chunk c of a group's 8 keys forms one 1 KB region, key by key, the
+// key's 16-byte pieces XOR-swizzled inside its 128 bytes. Tiles are filled
+// by direct global->LDS loads one tile ahead into a second buffer, one load
+// per (group, chunk): 8 whole cache lines, each lane fetching from its own
+// key's row, so no row address passes through scalar registers.
 //
 // Per tile, wavefront w:
 //   scores   S^T = K Q^T for keys 0..31 and 32..63 of the tile (two 32x32
@@ -61,21 +63,30 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kRowsWG = 128;  // query rows per workgroup (4 wavefronts x 32)
 constexpr int kKT = 64;       // keys per tile
-constexpr int kLatRow = 1024; // bytes of one key's latent part in LDS (64 pieces of 16 B)
-constexpr int kRopeRow = 128; // bytes of one key's rope part in LDS (8 pieces of 16 B)
-constexpr int kTileLat = kKT * kLatRow;
-constexpr int kTileBytes = kTileLat + kKT * kRopeRow;  // 73,728 bytes per tile buffer
+constexpr int kGK = 8;                                 // keys per staging group
+constexpr int kChunk = 128;                            // bytes of one key in one chunk (a cache line)
+constexpr int kChunks = (2 * kDKey) / kChunk;          // 9 chunks per key: 8 latent, 1 rope
+constexpr int kChunkBytes = kGK * kChunk;              // one chunk of a group's 8 keys: 1 KB
+constexpr int kGroupBytes = kChunks * kChunkBytes;     // 9 KB per group
+constexpr int kTileBytes = (kKT / kGK) * kGroupBytes;  // 73,728 bytes per tile buffer
+constexpr int kRopeRow = 128;                          // bytes of one query row's rope part in LDS
 constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
 constexpr int kSSteps = 2 * kQSteps;                   // score MFMAs per tile (two key blocks)
 constexpr int kVSteps = 64;                            // value MFMAs per tile (16 entry blocks x 4 key steps)
 constexpr int kSRing = 4;                              // score operand reads in flight
 constexpr int kVRing = 4;                              // value steps in flight (two reads each)
 
-// Piece swizzle of key k: key bits 0..1 to piece bits 2..3, key bits 2..3
-// to piece bits 0..1 (see the 64-row kernel: a permutation over any 16
-// consecutive keys, and 16 distinct slots for each transposed read cycle).
-__host__ __device__ constexpr int piece_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
-constexpr int kSwzHi = piece_swz(8) ^ piece_swz(0);  // swz(k + 8) ^ swz(k) for k % 16 < 8
+// Piece swizzle: position j of key k's 128 bytes in a chunk holds piece
+// j ^ xsw(k), xsw(k) = the three bits of (k % 16) / 2 in reverse order. A
+// key's line lands on bank half k % 2 (128-byte lines, 256 bytes of banks),
+// so the reads are conflict free when
+//   score reads (16 lanes, 16 keys, one piece each): xsw over the 8 keys of
+//     one parity among 16 consecutive keys is a permutation of 0..7;
+//   score reads paired across lane halves (keys k < 8 read pieces j and
+//     j ^ 1): xsw / 2 differs between the 4 keys of one parity;
+//   transposed value reads (keys 2m and 2m + 2, m even, four pieces each):
+//     xsw(2m) ^ xsw(2m + 2) = 4 puts them on disjoint position sets.
+__host__ __device__ constexpr int xsw(int k) { return ((k & 2) << 1) | ((k & 4) >> 1) | ((k >> 3) & 1); }
 
 template <int I>
 struct Int {
@@ -227,29 +238,14 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Direct-to-LDS staging of one 64-key tile, one load at a time over the
-// previous tile's score MFMAs. ra_lo/ra_hi hold, in lane k, the cache-row
-// address of the tile's key k.
-//   latent: key k = 16 wave + u; the row address goes to scalar registers as
-//           the load's base and lane l loads piece l ^ swz(k) into LDS piece
-//           l of the key's 1024-byte latent row;
-//   rope:   keys 8v..8v+7 (v = 2 wave + u): lane l serves key 8v + l/8 and
-//           stores its piece (l%8) ^ (k%8) at position l%8 of the key's
-//           128-byte rope row; `row` is that key's cache row.
-__device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
-  const int k = 16 * wave + u;
-  const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
-  // (an unsigned 32-bit offset: the load takes the uniform row address as its
-  // scalar base and one offset register, with no 64-bit address arithmetic)
-  const char* src = reinterpret_cast<const char*>(row_addr) + (uint32_t)((lane ^ piece_swz(k)) << 4);
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 0);
-}
-
-__device__ __forceinline__ void stage_rope(char* dst, const char* row, int wave, int lane, int u) {
-  const int v = 2 * wave + u;
-  const char* src = row + kDLatent * 2 + 16 * ((lane & 7) ^ (lane >> 3));
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
+// Direct-to-LDS staging load of chunk c of group G's 8 keys (1 KB). `a`
+// is, in lane l, the address in its cache row's chunk 0 of the piece that
+// lane stores: key 8G + l / 8, piece (l % 8) ^ xsw(key), at position l % 8
+// of the key's 128 bytes. The loads of a tile go one at a time over the
+// previous tile's score MFMAs.
+template <int C>
+__device__ __forceinline__ void stage_chunk(char* dst, const char* a, int G) {
+  __builtin_amdgcn_global_load_lds(a + kChunk * C, TVMLA_LDS(void, dst + G * kGroupBytes + C * kChunkBytes), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -387,60 +383,61 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   };
 
   const int ntiles = (end - start + kKT - 1) / kKT;
+  // Wavefront w stages groups 2w and 2w + 1 of each tile. gs0 / gs1: in lane
+  // l, the slot of the key that lane serves in group 2w / 2w + 1 of the tile
+  // being staged; `slot_reg` holds, in lane k, the slot of a tile's key k.
   int slot_reg = slot_of(start + lane);
-  auto row_address = [&](int slot, uint32_t& lo, uint32_t& hi) {
-    const uint64_t a = (uint64_t)(uintptr_t)(kvb + (int64_t)slot * row_bytes);
-    lo = (uint32_t)a;
-    hi = (uint32_t)(a >> 32);
+  int gs0, gs1;
+  // (ds_bpermute with the byte index of the source lane; the lane index is
+  // recomputed here rather than held across the tile loop)
+  auto group_slots = [&](int slots) {
+    const int ln = opaque(lane);
+    gs0 = __builtin_amdgcn_ds_bpermute(4 * (16 * wave + (ln >> 3)), slots);
+    gs1 = __builtin_amdgcn_ds_bpermute(4 * (16 * wave + kGK + (ln >> 3)), slots);
   };
+  auto chunk0 = [&](int slot, int u, int ln) -> const char* {
+    return kvb + (int64_t)slot * row_bytes + 16 * ((ln & 7) ^ xsw(kGK * u + (ln >> 3)));
+  };
+  group_slots(slot_reg);
   {
-    uint32_t lo, hi;
-    row_address(slot_reg, lo, hi);
-#pragma unroll
-    for (int u = 0; u < kKT / 4; ++u) stage_key(kb0, lo, hi, wave, lane, u);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      stage_rope(kb0, kvb + (int64_t)__shfl(slot_reg, 8 * (2 * wave + u) + (lane >> 3), 64) * row_bytes, wave, lane,
-                 u);
+    const char* a0 = chunk0(gs0, 0, lane);
+    const char* a1 = chunk0(gs1, 1, lane);
+    static_for<0, kChunks>([&](auto c_) { stage_chunk<decltype(c_)::value>(kb0, a0, 2 * wave); });
+    static_for<0, kChunks>([&](auto c_) { stage_chunk<decltype(c_)::value>(kb0, a1, 2 * wave + 1); });
   }
   load_mask(start);
   slot_reg = slot_of(start + kKT + lane);
+  group_slots(slot_reg);
 
   auto body = [&](int tile, const char* cur, char* nxt) {
     const int p0 = start + tile * kKT;
     const int ln = opaque(lane);
     const uint64_t vis = visible_bits(p0);
     load_mask(p0 + kKT);  // on the last tile these re-read clamped, valid bytes
-    const int slot_cur = slot_reg;
+    // next tile's staging address: chunk 0 of group 2w's rows (group 2w +
+    // 1's is formed when its first load is due)
+    const char* sa = chunk0(gs0, 0, ln);
     slot_reg = slot_of(p0 + 2 * kKT + lane);
-    uint32_t ra_lo, ra_hi;  // lane k: cache row address of the next tile's key k
-    row_address(slot_cur, ra_lo, ra_hi);
-    const int rslot0 = __shfl(slot_cur, 16 * wave + (ln >> 3), 64);
-    const int rslot1 = __shfl(slot_cur, 16 * wave + 8 + (ln >> 3), 64);
 
     // ---- S^T = K Q^T, key block kb = n / 36, k-step ks = n % 36 (block 0's
     // chain, then block 1's). Score operand of lane (hf, col): key 32kb +
-    // col, latent piece 2ks + hf stored at (2ks + hf) ^ swz(col) =
-    // 16(ks / 8) + ((2(ks % 8)) ^ sq), sq = swz(col) ^ hf; rope k-step
-    // 32 + c reads rope piece 2c + hf stored at (2c + hf) ^ (col % 8).
-    // The eight latent address patterns and two rope ones are registers;
-    // block, piece group and rope block are immediate offsets.
+    // col (group 4kb + col / 8, line col % 8), piece 2ks + hf (rope for ks
+    // >= 32): chunk ks / 4, position (2(ks % 4) + hf) ^ xsw(col). Four
+    // address patterns (ks % 4) are registers; block and chunk are
+    // immediate offsets.
     const uint32_t cur_lds = (uint32_t)(uintptr_t)TVMLA_LDS(const char, cur);
     const int lcol = ln & 31, lhf = ln >> 5;
-    const int sq = piece_swz(lcol) ^ lhf;
-    const uint32_t kbase = cur_lds + lcol * kLatRow;
-    const uint32_t rbase = cur_lds + kTileLat + lcol * kRopeRow;
-    const int rsw = lhf ^ (lcol & 7);
+    const int sx = xsw(lcol & 15) ^ lhf;
+    const uint32_t sbase = cur_lds + (lcol >> 3) * kGroupBytes + (lcol & 7) * kChunk;
+    const int rsw = lhf ^ (lcol & 7);  // rope pieces of the queries (their own LDS rows)
     auto saddr = [&](auto n_) -> uint32_t {
       constexpr int n = decltype(n_)::value, ks = n % kQSteps;
-      if constexpr (ks < 32)
-        return kbase + (((2 * (ks % 8)) ^ sq) << 4);
-      else
-        return rbase + (((2 * (ks - 32)) ^ rsw) << 4);
+      return sbase + (((2 * (ks % 4)) ^ sx) << 4);
     };
     auto sread = [&](auto n_) -> bf16x8_t {
       constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
-      constexpr int off = ks < 32 ? kb * 32 * kLatRow + 256 * (ks / 8) : kb * 32 * kRopeRow;
+      constexpr int off = kb * (32 / kGK) * kGroupBytes + (ks / 4) * kChunkBytes;
+      static_assert(off < 65536, "LDS offsets are 16-bit");
       return read_b128<off>(saddr(n_));
     };
 
@@ -529,22 +526,25 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     // ---- value product O^T += V^T P^T, step n: key step q = n / 16 (keys
     // 16q ..), entry block db = n % 16. Key step q = 2h + c takes score
     // registers 8c .. 8c+7 of block h, i.e. keys 16q + 8(m/4) + 4hf + m%4
-    // (m = 0..7), so the V^T operand holds V rows 16q + 4hf + vr .. (lo) and
-    // +8 (hi): lane group row vr = (lane & 15) / 4 reads latent entries
-    // 32db + 16 g1 + 4(lane & 3) .. +3 (g1 = lane bit 4), piece 4db + vpl
-    // (vpl = 2 g1 + (lane & 3) / 2) stored at 16(db / 4) + ((4(db % 4) + vpl)
-    // ^ swz(vr + 8x)).
+    // (m = 0..7), so the V^T operand holds V rows 16q + vr (lo) and 16q +
+    // vr + 8 (hi), vr = 4hf + (lane & 15) / 4: the lane reads latent entries
+    // 32db + 16 g1 + 4(lane & 3) .. +3 (g1 = lane bit 4), i.e. piece 4db +
+    // vpl (vpl = 2 g1 + (lane & 3) / 2), byte 8(lane & 1) -- of key 16q + vr
+    // + 8x: group 2q + x, line vr, chunk db / 2, position (4(db % 2) + vpl)
+    // ^ xsw(vr + 8x). Four address patterns (x, db % 2) are registers.
     const int vr = 4 * lhf + ((ln & 15) >> 2);
-    const int vt = (2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ piece_swz(vr);
-    const uint32_t vbase = cur_lds + vr * kLatRow + 8 * (ln & 1);
-    auto vaddr_lo = [&](int d4) -> uint32_t { return vbase + ((vt ^ (4 * d4)) << 4); };
-    auto vaddr_hi = [&](int d4) -> uint32_t { return vbase + ((vt ^ (4 * d4) ^ kSwzHi) << 4); };
+    const int vpl = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+    const uint32_t vbase = cur_lds + vr * kChunk + 8 * (ln & 1);
+    auto vaddr = [&](int x, int d2) -> uint32_t {
+      return vbase + x * kGroupBytes + (((4 * d2 + vpl) ^ xsw(vr + kGK * x)) << 4);
+    };
     i16x4_t vlo[kVRing], vhi[kVRing];
     auto vread = [&](auto n_) {
       constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
-      constexpr int off = 16 * q * kLatRow + 256 * (db / 4);
-      vlo[n % kVRing] = read_tr<off>(vaddr_lo(db % 4));
-      vhi[n % kVRing] = read_tr<off + 8 * kLatRow>(vaddr_hi(db % 4));
+      constexpr int off = 2 * q * kGroupBytes + (db / 2) * kChunkBytes;
+      static_assert(off < 65536, "LDS offsets are 16-bit");
+      vlo[n % kVRing] = read_tr<off>(vaddr(0, db % 2));
+      vhi[n % kVRing] = read_tr<off>(vaddr(1, db % 2));
     };
     // value steps [B, E); `side(i)` runs between steps (i = step - B)
     auto pv_steps = [&](auto b_, auto e_, auto&& side) {
@@ -564,8 +564,8 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
 
     // ---- scores. Block 0's softmax pieces ride along block 1's MFMAs
     // (from two MFMAs after block 0's last, when its results are written).
-    // The next tile's sixteen latent loads go one per four MFMAs, the rope
-    // loads after the last operand wait.
+    // The next tile's 18 staging loads (two groups x 9 chunks) go one per
+    // four MFMAs.
     // The rope part of the queries is read from LDS four k-steps before the
     // block's rope steps, right after that step's operand read, so the
     // operand wait of the first rope step covers it as well.
@@ -575,7 +575,11 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     f32x16_t sacc[2];
     static_for<0, kSSteps>([&](auto n_) {
       constexpr int n = decltype(n_)::value, kb = n / kQSteps, ks = n % kQSteps;
-      if constexpr (n % 4 == 1 && n / 4 < 16) stage_key(nxt, ra_lo, ra_hi, wave, ln, n / 4);
+      if constexpr (n % 4 == 1 && n / 4 < 2 * kChunks) {
+        constexpr int j = n / 4;
+        if constexpr (j == kChunks) sa = chunk0(opaque(gs1), 1, ln);
+        stage_chunk<j % kChunks>(nxt, sa, 2 * wave + j / kChunks);
+      }
       bf16x8_t& kf = ring[n % kSRing];
       constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
       // (the rope operands were read right after step 28's operand read, so
@@ -610,8 +614,6 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       if constexpr (k0 == kProbGaps - 1) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
       __builtin_amdgcn_sched_barrier(0);
     });
-    stage_rope(nxt, kvb + (int64_t)rslot0 * row_bytes, wave, ln, 0);
-    stage_rope(nxt, kvb + (int64_t)rslot1 * row_bytes, wave, ln, 1);
 
     // Reference max. A row whose max exceeds its reference by more than
     // fold_log2 takes a new reference: at once if it has accumulated nothing
@@ -669,6 +671,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     });
     l_part += psum[0] + psum[1];
     pv_steps(Int<32>{}, Int<64>{}, [](auto) {});
+    group_slots(slot_reg);  // for the tile after next, staged by the next tile
   };
   for (int tile = 0; tile < ntiles; ++tile) {
     tile_barrier();  // tile in LDS; every wavefront is done with the previous one
@@ -688,7 +691,9 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     TVMLA_O_DRAIN(o);
   }
   const float lsum = l_fold * beta + l_part;
-  const float l = lsum + __shfl_xor(lsum, 32, 64);
+  // the row's two lane halves: lane k < 32 adds lane k + 32's share, lane k + 32 lane k's
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+  const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   if (r >= R) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* dst = partial_bf16(p.o_part, pr) + 4 * opaque(hf);  // the row's output as bf16 (the slot's first 1 KB)
