@@ -141,17 +141,24 @@ __device__ __forceinline__ i16x4_t read_tr(uint32_t addr) {
 // what 8 passes need), and "s_nop 1" (2 wait states) in front of an MFMA
 // whose operand may have just been written by a vector ALU instruction.
 //
-// The operand MFMAs wait for their LDS operand in the same statement
+// The operand MFMAs wait for their LDS operands in the same statement
 // ("s_waitcnt lgkmcnt(n)": at most n LDS operations of this wavefront still
-// outstanding). A separate wait statement would have to name the operand
-// as an output, and the compiler then guards every MFMA behind it with a
-// hazard nop as if a vector ALU instruction had just written the operand.
+// outstanding), once per pair of steps: the even step's MFMA waits for its
+// own operand and the odd step's, and the odd step's MFMA (the _NW forms)
+// issues without a wait. A separate wait statement would have to name the
+// operand as an output, and the compiler then guards every MFMA behind it
+// with a hazard nop as if a vector ALU instruction had just written the
+// operand.
 #define TVMLA_MFMA_S_FIRST(n, acc, a, q)                                                             \
   asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) \
                : "v"(a), "v"(q), "n"(n))
 #define TVMLA_MFMA_S(n, acc, a, q)                                                                            \
   asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q), \
                "n"(n))
+#define TVMLA_MFMA_S_NW(acc, a, q) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q))
+#define TVMLA_MFMA_O_NW(acc, a, p) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p))
 #define TVMLA_MFMA_O(n, acc, a, p)                                                                            \
   asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(p), \
                "n"(n))
@@ -298,7 +305,9 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
 
   // Q^T operands: the lane's row, key entries [16ks + 8hf, +8): the 32
   // latent k-steps in registers, the 4 rope k-steps in LDS (rope piece
-  // 2c + hf of local row x at position (2c + hf) ^ (x % 8)).
+  // 2c + hf of local row x at position (2c + hf) ^ xsw(x % 16): the rows are
+  // 128 bytes apart like a chunk's keys, so the key swizzle keeps the reads
+  // conflict free).
   bf16x8_t qf[kDLatent / 16];
   {
     const uint16_t* qn = static_cast<const uint16_t*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head + 8 * hf;
@@ -308,7 +317,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     char* qrow = qrope + (32 * wave + col) * kRopeRow;
 #pragma unroll
     for (int c = 0; c < kDRope / 16; ++c)
-      *reinterpret_cast<uint4*>(qrow + (((2 * c + hf) ^ (col & 7)) << 4)) =
+      *reinterpret_cast<uint4*>(qrow + (((2 * c + hf) ^ xsw(col & 15)) << 4)) =
           *reinterpret_cast<const uint4*>(qr + 16 * c);
   }
 
@@ -429,7 +438,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     const int lcol = ln & 31, lhf = ln >> 5;
     const int sx = xsw(lcol & 15) ^ lhf;
     const uint32_t sbase = cur_lds + (lcol >> 3) * kGroupBytes + (lcol & 7) * kChunk;
-    const int rsw = lhf ^ (lcol & 7);  // rope pieces of the queries (their own LDS rows)
+    const int rsw = lhf ^ xsw(lcol & 15);  // rope pieces of the queries (their own LDS rows)
     auto saddr = [&](auto n_) -> uint32_t {
       constexpr int n = decltype(n_)::value, ks = n % kQSteps;
       return sbase + (((2 * (ks % 4)) ^ sx) << 4);
@@ -551,11 +560,16 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       constexpr int B = decltype(b_)::value, E = decltype(e_)::value;
       static_for<B, E>([&](auto n_) {
         constexpr int n = decltype(n_)::value, q = n / 16, db = n % 16;
-        constexpr int ahead = 2 * (kVSteps - 1 - n < kVRing - 1 ? kVSteps - 1 - n : kVRing - 1);
+        // even steps wait for this step's and the next step's operands: at
+        // most the reads of the steps after n + 1 stay outstanding
+        constexpr int ahead = 2 * (kVSteps - 2 - n < kVRing - 2 ? kVSteps - 2 - n : kVRing - 2);
+        static_assert(kVSteps % 2 == 0 && kVRing >= 2, "value steps wait in pairs");
         if constexpr (db == 0)  // pf[q] is vector-ALU output: two wait states before an MFMA reads it
           TVMLA_MFMA_O_NOP(ahead, o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
-        else
+        else if constexpr (n % 2 == 0)
           TVMLA_MFMA_O(ahead, o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
+        else
+          TVMLA_MFMA_O_NW(o[db], cat4(vlo[n % kVRing], vhi[n % kVRing]), pf[q]);
         if constexpr (n + kVRing < kVSteps) vread(Int<n + kVRing>{});
         side(Int<n - B>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -581,15 +595,19 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         stage_chunk<j % kChunks>(nxt, sa, 2 * wave + j / kChunks);
       }
       bf16x8_t& kf = ring[n % kSRing];
-      constexpr int ahead = kSSteps - 1 - n < kSRing - 1 ? kSSteps - 1 - n : kSRing - 1;
-      // (the rope operands were read right after step 28's operand read, so
-      // step 32's wait covers them too)
+      // even steps wait for this step's and the next step's operands (at
+      // most the reads of the steps after n + 1 outstanding); the rope
+      // operands were read right after step 32's operand read, so step 32's
+      // wait covers them too
+      constexpr int ahead = kSSteps - 2 - n < kSRing - 2 ? kSSteps - 2 - n : kSRing - 2;
+      static_assert(kQSteps % 2 == 0, "score steps wait in pairs within each block");
+      const bf16x8_t& qop = ks < 32 ? qf[ks < 32 ? ks : 0] : qrf[ks < 32 ? 0 : ks - 32];
       if constexpr (ks == 0)
         TVMLA_MFMA_S_FIRST(ahead, sacc[kb], kf, qf[0]);
-      else if constexpr (ks < 32)
-        TVMLA_MFMA_S(ahead, sacc[kb], kf, qf[ks]);
+      else if constexpr (n % 2 == 0)
+        TVMLA_MFMA_S(ahead, sacc[kb], kf, qop);
       else
-        TVMLA_MFMA_S(ahead, sacc[kb], kf, qrf[ks - 32]);
+        TVMLA_MFMA_S_NW(sacc[kb], kf, qop);
       if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
       static_assert(kSRing == 4, "the rope operand reads assume four operand reads in flight");
       if constexpr (ks == 32 - kSRing) {
