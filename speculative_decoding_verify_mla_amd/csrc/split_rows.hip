@@ -70,6 +70,8 @@ constexpr int kChunkBytes = kGK * kChunk;              // one chunk of a group's
 constexpr int kGroupBytes = kChunks * kChunkBytes;     // 9 KB per group
 constexpr int kTileBytes = (kKT / kGK) * kGroupBytes;  // 73,728 bytes per tile buffer
 constexpr int kRopeRow = 128;                          // bytes of one query row's rope part in LDS
+constexpr int kQRow = 2 * kDLatent;                    // bytes of one query row's latent part (1 KB)
+static_assert(2 * 32 * kQRow <= kTileBytes, "two wavefronts' query rows fit in one tile buffer");
 constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
 constexpr int kSSteps = 2 * kQSteps;                   // score MFMAs per tile (two key blocks)
 constexpr int kVSteps = 64;                            // value MFMAs per tile (16 entry blocks x 4 key steps)
@@ -87,6 +89,9 @@ constexpr int kVRing = 4;                              // value steps in flight 
 //   transposed value reads (keys 2m and 2m + 2, m even, four pieces each):
 //     xsw(2m) ^ xsw(2m + 2) = 4 puts them on disjoint position sets.
 __host__ __device__ constexpr int xsw(int k) { return ((k & 2) << 1) | ((k & 4) >> 1) | ((k >> 3) & 1); }
+// Piece swizzle of query row j (0..31) in LDS during the prologue: rows 0..7
+// of 16 get even values 0..14, rows 8..15 odd ones.
+__host__ __device__ constexpr int qsw(int j) { return ((j & 7) << 1) | ((j >> 3) & 1); }
 
 template <int I>
 struct Int {
@@ -303,23 +308,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const int h = rr - i * p.num_heads;
   const int64_t t = tb + i;
 
-  // Q^T operands: the lane's row, key entries [16ks + 8hf, +8): the 32
-  // latent k-steps in registers, the 4 rope k-steps in LDS (rope piece
-  // 2c + hf of local row x at position (2c + hf) ^ xsw(x % 16): the rows are
-  // 128 bytes apart like a chunk's keys, so the key swizzle keeps the reads
-  // conflict free).
-  bf16x8_t qf[kDLatent / 16];
-  {
-    const uint16_t* qn = static_cast<const uint16_t*>(p.q_nope) + t * p.qn_stride_tok + h * p.qn_stride_head + 8 * hf;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + t * p.qr_stride_tok + h * p.qr_stride_head + 8 * hf;
-#pragma unroll
-    for (int ks = 0; ks < kDLatent / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qn + 16 * ks));
-    char* qrow = qrope + (32 * wave + col) * kRopeRow;
-#pragma unroll
-    for (int c = 0; c < kDRope / 16; ++c)
-      *reinterpret_cast<uint4*>(qrow + (((2 * c + hf) ^ xsw(col & 15)) << 4)) =
-          *reinterpret_cast<const uint4*>(qr + 16 * c);
-  }
+  bf16x8_t qf[kDLatent / 16];  // Q^T operands of the lane's row (loaded in the prologue below)
 
   f32x16_t o[16];  // O^T blocks: latent entries [32db, 32db + 32) x the 32 rows
 #pragma unroll
@@ -395,7 +384,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   // Wavefront w stages groups 2w and 2w + 1 of each tile. gs0 / gs1: in lane
   // l, the slot of the key that lane serves in group 2w / 2w + 1 of the tile
   // being staged; `slot_reg` holds, in lane k, the slot of a tile's key k.
-  int slot_reg = slot_of(start + lane);
+  int slot_reg;
   int gs0, gs1;
   // (ds_bpermute with the byte index of the source lane; the lane index is
   // recomputed here rather than held across the tile loop)
@@ -407,15 +396,65 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   auto chunk0 = [&](int slot, int u, int ln) -> const char* {
     return kvb + (int64_t)slot * row_bytes + 16 * ((ln & 7) ^ xsw(kGK * u + (ln >> 3)));
   };
-  group_slots(slot_reg);
+  // ---- prologue. The first tile's group slots (loaded directly, no lane
+  // exchange), the second tile's slots and the first tile's mask bytes go
+  // out first; then the queries; then, once every wavefront holds its
+  // queries, the first tile's staging.
+  gs0 = slot_of(start + 16 * wave + (lane >> 3));
+  gs1 = slot_of(start + 16 * wave + kGK + (lane >> 3));
+  slot_reg = slot_of(start + kKT + lane);
+  load_mask(start);
+
+  // Q^T operands: the lane's row, key entries [16ks + 8hf, +8).
+  //   latent (32 k-steps, kept in registers for the whole split): the
+  //     wavefront's 32 rows pass through LDS -- the tile buffers, free until
+  //     the first tile is staged, 32 KB per wavefront -- with one
+  //     direct-to-LDS load per whole 1 KB row (8 full cache lines; loading
+  //     the operand layout straight from memory takes 32 bytes of 32 rows
+  //     per load, four times the memory requests), then 32 LDS reads in the
+  //     operand layout. Piece P of row j sits at position P ^ qsw(j):
+  //     conflict free for 16 lanes of one half (16 rows) and for 8 rows of
+  //     both halves (even against odd positions).
+  //   rope (4 k-steps, read from LDS at each tile's rope steps): rope piece
+  //     2c + hf of local row x at position (2c + hf) ^ xsw(x % 16) of its
+  //     128-byte row; the rows are 128 bytes apart like a chunk's keys, so
+  //     the key swizzle keeps the reads conflict free.
+  {
+    char* qlat = (wave < 2 ? kb0 : kb1) + (wave & 1) * (32 * kQRow);
+    const int x0 = g * kRowsWG + 32 * wave;  // the wavefront's first row (rows past R - 1 repeat row R - 1)
+    int rj = min(x0, R - 1);
+    int ij = rj / p.num_heads;
+    int hj = rj - ij * p.num_heads;
+    const uint16_t* qn0 = static_cast<const uint16_t*>(p.q_nope);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const char* row = reinterpret_cast<const char*>(qn0 + (tb + ij) * p.qn_stride_tok + (int64_t)hj * p.qn_stride_head);
+      __builtin_amdgcn_global_load_lds(row + 16 * (lane ^ qsw(j)), TVMLA_LDS(void, qlat + j * kQRow), 16, 0, 0);
+      if (x0 + j + 1 < R && ++hj == p.num_heads) {
+        hj = 0;
+        ++ij;
+      }
+    }
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + t * p.qr_stride_tok + h * p.qr_stride_head + 8 * hf;
+    char* qrow = qrope + (32 * wave + col) * kRopeRow;
+#pragma unroll
+    for (int c = 0; c < kDRope / 16; ++c)
+      *reinterpret_cast<uint4*>(qrow + (((2 * c + hf) ^ xsw(col & 15)) << 4)) =
+          *reinterpret_cast<const uint4*>(qr + 16 * c);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's rows are in LDS
+    const char* qmine = qlat + col * kQRow;
+#pragma unroll
+    for (int ks = 0; ks < kDLatent / 16; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qmine + 16 * ((2 * ks + hf) ^ qsw(col)));
+  }
+  lds_barrier();  // every wavefront holds its queries: the tile buffers are free
+
   {
     const char* a0 = chunk0(gs0, 0, lane);
     const char* a1 = chunk0(gs1, 1, lane);
     static_for<0, kChunks>([&](auto c_) { stage_chunk<decltype(c_)::value>(kb0, a0, 2 * wave); });
     static_for<0, kChunks>([&](auto c_) { stage_chunk<decltype(c_)::value>(kb0, a1, 2 * wave + 1); });
   }
-  load_mask(start);
-  slot_reg = slot_of(start + kKT + lane);
   group_slots(slot_reg);
 
   auto body = [&](int tile, const char* cur, char* nxt) {
