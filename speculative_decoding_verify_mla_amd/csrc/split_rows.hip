@@ -71,6 +71,8 @@ constexpr int kGroupBytes = kChunks * kChunkBytes;     // 9 KB per group
 constexpr int kTileBytes = (kKT / kGK) * kGroupBytes;  // 73,728 bytes per tile buffer
 constexpr int kRopeRow = 128;                          // bytes of one query row's rope part in LDS
 constexpr int kQRow = 2 * kDLatent;                    // bytes of one query row's latent part (1 KB)
+constexpr int kORow = kQRow + 8;                       // LDS stride of an output row in the epilogue
+static_assert(2 * 32 * kORow <= kTileBytes, "two wavefronts' output rows fit in one tile buffer");
 static_assert(2 * 32 * kQRow <= kTileBytes, "two wavefronts' query rows fit in one tile buffer");
 constexpr int kQSteps = kDKey / 16;                    // 36 k-steps of 16 over the key width
 constexpr int kSSteps = 2 * kQSteps;                   // score MFMAs per tile (two key blocks)
@@ -751,17 +753,40 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   // the row's two lane halves: lane k < 32 adds lane k + 32's share, lane k + 32 lane k's
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
   const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  if (r >= R) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* dst = partial_bf16(p.o_part, pr) + 4 * opaque(hf);  // the row's output as bf16 (the slot's first 1 KB)
+  if (hf == 0 && r < R) p.lse_part[pr] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+
+  // The rows' normalised outputs as bf16 (each row slot's first 1 KB) go
+  // out as two stores of 512 contiguous bytes per row: written straight
+  // from the accumulator layout, a store would take 16 bytes of each of 32
+  // rows, eight times the memory requests. So they pass through LDS: once
+  // every wavefront is past its last tile the tile buffers are free, and the
+  // wavefront's 32 rows take 33 KB, row j at j * 1032 bytes with its 8-byte
+  // unit u (entries 4u .. 4u+3) at 8u. The 129-unit row stride puts unit u
+  // of the 32 rows on 32 distinct bank pairs (row j's on pair (j + u) mod
+  // 32), and a row's read-back (lane l: units l and l + 64) covers
+  // consecutive units.
+  lds_barrier();
+  char* obuf = (wave < 2 ? kb0 : kb1) + (wave & 1) * (32 * kORow);
+  {
+    char* orow = obuf + col * kORow + 8 * hf;
 #pragma unroll
-  for (int db = 0; db < 16; ++db)
+    for (int db = 0; db < 16; ++db)
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg)
-      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * jg) =
-          pack_bf16x4(o[db][4 * jg + 0] * inv, o[db][4 * jg + 1] * inv, o[db][4 * jg + 2] * inv,
-                      o[db][4 * jg + 3] * inv);
-  if (hf == 0) p.lse_part[pr] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+      for (int jg = 0; jg < 4; ++jg)
+        *reinterpret_cast<uint2*>(orow + 64 * db + 16 * jg) =
+            pack_bf16x4(o[db][4 * jg + 0] * inv, o[db][4 * jg + 1] * inv, o[db][4 * jg + 2] * inv,
+                        o[db][4 * jg + 3] * inv);
+  }
+  const uint32_t pr0 = pr - col;  // the wavefront's first partial-result row
+  for (int j = 0; j < rows_valid; ++j) {
+    const char* src = obuf + j * kORow + 8 * lane;
+    const uint2 v0 = *reinterpret_cast<const uint2*>(src);
+    const uint2 v1 = *reinterpret_cast<const uint2*>(src + 512);
+    uint16_t* dst = partial_bf16(p.o_part, pr0 + j) + 4 * lane;
+    *reinterpret_cast<uint2*>(dst) = v0;
+    *reinterpret_cast<uint2*>(dst + 256) = v1;
+  }
 }
 
 }  // namespace
