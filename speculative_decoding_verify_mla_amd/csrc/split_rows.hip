@@ -255,11 +255,15 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 // Direct-to-LDS staging load of chunk c of group G's 8 keys (1 KB). `a`
 // is, in lane l, the address in its cache row's chunk 0 of the piece that
 // lane stores: key 8G + l / 8, piece (l % 8) ^ xsw(key), at position l % 8
-// of the key's 128 bytes. The loads of a tile go one at a time over the
-// previous tile's score MFMAs.
+// of the key's 128 bytes. The chunk's 128c bytes are the load's immediate
+// offset, which the hardware adds to the global and to the LDS address
+// alike, so the LDS base given is 1024c - 128c past the group's (this spares
+// a 64-bit address add per load). The loads of a tile go one at a time over
+// the previous tile's score MFMAs.
 template <int C>
 __device__ __forceinline__ void stage_chunk(char* dst, const char* a, int G) {
-  __builtin_amdgcn_global_load_lds(a + kChunk * C, TVMLA_LDS(void, dst + G * kGroupBytes + C * kChunkBytes), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(a, TVMLA_LDS(void, dst + G * kGroupBytes + C * (kChunkBytes - kChunk)), 16,
+                                   kChunk * C, 0);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
