@@ -548,9 +548,11 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     // Probability j of block h against mu = -m_ref (0 while m_ref = -inf):
     // F (the fma into pt[j]), E (exp2 in place), S (the running sum, and for
     // odd j the pair packed into the P^T operand). prob_stage(h, k, mu) is
-    // gap k of the pipeline: S(k-2), E(k-1), F(k); gaps 0..17 cover j =
-    // 0..15, each stage one gap after the one it needs. The sum runs over
-    // j = 0..15 in order as before.
+    // step k of the pipeline: S(k-2), E(k-1), F(k); steps 0..17 cover j =
+    // 0..15, each stage one step after the one it needs. The sum runs over
+    // j = 0..15 in order as before. The steps go into two of every three
+    // MFMA gaps (27 gaps), which leaves the exp2 (a quarter-rate
+    // instruction) more room beside the MFMAs than three stages every gap.
     float pt[16];
     auto prob_f = [&](int h, int j, float mu) { pt[j] = __builtin_fmaf(sm[h][j], scale2, mu); };
     auto prob_e = [&](int j) { pt[j] = __builtin_amdgcn_exp2f(pt[j]); };
@@ -669,12 +671,13 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       }
       if constexpr (i >= 1 && i <= kMaxParts) max_part(0, i - 1);
       constexpr int k0 = i - (kMaxParts + 1);  // gap of block 0's probability pipeline
-      if constexpr (k0 >= 0 && k0 < kProbGaps) prob_stage(0, k0, mu0);
-      static_assert(kQSteps + 2 + kMaxParts + kProbGaps <= kSSteps, "block 0's softmax must fit under block 1's MFMAs");
+      constexpr int g0 = k0 - k0 / 3;  // pipeline step of this gap (every third gap empty)
+      if constexpr (k0 >= 0 && k0 % 3 != 2 && g0 < kProbGaps) prob_stage(0, g0, mu0);
+      static_assert(kQSteps + 2 + kMaxParts + (3 * kProbGaps) / 2 <= kSSteps, "block 0's softmax must fit under block 1's MFMAs");
       // Keep them here: the reference decision below recomputes them when
       // the reference moves, and the compiler would otherwise sink them into
       // the other branch, after the last score MFMA.
-      if constexpr (k0 == kProbGaps - 1) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
+      if constexpr (k0 % 3 != 2 && g0 == kProbGaps - 1) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -730,7 +733,8 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     static_for<0, kVRing>([&](auto x_) { vread(x_); });
     pv_steps(Int<0>{}, Int<32>{}, [&](auto i_) {
       constexpr int i = decltype(i_)::value;
-      if constexpr (i >= 1 && i < 1 + kProbGaps) prob_stage(1, i - 1, mu1);
+      constexpr int k1 = i - 1, g1 = k1 - k1 / 3;
+      if constexpr (k1 >= 0 && k1 % 3 != 2 && g1 < kProbGaps) prob_stage(1, g1, mu1);
     });
     l_part += psum[0] + psum[1];
     pv_steps(Int<32>{}, Int<64>{}, [](auto) {});
