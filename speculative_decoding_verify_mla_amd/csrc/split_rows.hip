@@ -34,9 +34,13 @@
 // Against the 64-row kernel this halves the staging loads and tile barriers
 // per row and drops the probability exchange; in exchange every wavefront
 // reads the whole tile from LDS (about 136 KB per wavefront per tile).
+// Before the first tile and after the last one the tile buffers are free:
+// the queries come in, and the output rows go out, through them, so that
+// those memory accesses are whole rows rather than pieces of 32 rows.
 //
 // Split bounds, key slots, mask bytes and P_b follow page 1, "The Design
-// Emerges" (chunk = ceil(N / nsplit), empty split returns at once; slot from
+// Emerges" (chunk = ceil(N / nsplit), rounded up to whole 64-key tiles when
+// the caller asks for that; empty split returns at once; slot from
 // kv_indices for the prefix and out_cache_loc for draft keys; mask byte
 // custom_mask[mask_indptr[b] + i*N + p]; P_b from kv_indptr). The online
 // softmax (page 1, "Input Knowledge Required": running max, running sum,
