@@ -111,10 +111,12 @@ typedef enum {
 
 /*
  * fold_log2 (tvmla_verify_ex, _ragged, _partials): TVMLA_ALGO_ROWS keeps
- * each row's softmax against a reference max and folds its accumulator into
- * the row's workspace slot when the row's max outgrows that reference by
- * more than 2^fold_log2. A negative value selects the default, 16 (every
- * probability stays below 2^16); NaN is rejected with TVMLA_E_VALUE.
+ * each row's softmax against a reference max and moves the reference --
+ * folding the row's accumulator into its workspace slot -- when a block of
+ * keys would take a probability above 2^fold_log2 against it (the row's
+ * scaled max, in log2 units, outgrew the reference by more than fold_log2).
+ * A negative or infinite value selects the default, 16 (every probability
+ * stays below 2^16); NaN is rejected with TVMLA_E_VALUE.
  * Results are the same for any threshold up to rounding: only the number of
  * folds changes (small thresholds make folds frequent, which tests use to
  * exercise that path). Other algorithms ignore it.

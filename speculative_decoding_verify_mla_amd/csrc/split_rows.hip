@@ -84,6 +84,29 @@ constexpr int kVSteps = 64;                            // value MFMAs per tile (
 constexpr int kSRing = 4;                              // score operand reads in flight
 constexpr int kVRing = 4;                              // value steps in flight (two reads each)
 
+// LDS reads a wavefront issues in the score phase of a tile: kSRing operand
+// reads before step 0; after its MFMA, step m reads step m + kSRing's
+// operand, at k-step 32 - kSRing also the four rope pieces of the queries,
+// and in the last kVEarly steps the first value steps' operands (two reads
+// each).
+constexpr int kVEarly = 2;
+constexpr int s_reads_issued(int m) {
+  return (m + kSRing < kSSteps ? 1 : 0) + (m % kQSteps == 32 - kSRing ? kDRope / 16 : 0) + (m >= kSSteps - kVEarly ? 2 : 0);
+}
+// Reads issued after step r's operand read and before step n's MFMA.
+constexpr int s_reads_after(int r, int n) {
+  int c = 0;
+  if (r < kSRing) {
+    c = kSRing - 1 - r;
+    for (int m = 0; m < n; ++m) c += s_reads_issued(m);
+  } else {
+    c = s_reads_issued(r - kSRing) - 1;
+    for (int m = r - kSRing + 1; m < n; ++m) c += s_reads_issued(m);
+  }
+  return c;
+}
+static_assert(s_reads_after(3, 2) == 2 && s_reads_after(31, 30) == 6, "read counts");
+
 // Piece swizzle: position j of key k's 128 bytes in a chunk holds piece
 // j ^ xsw(k), xsw(k) = the three bits of (k % 16) / 2 in reverse order. A
 // key's line lands on bank half k % 2 (128-byte lines, 256 bytes of banks),
@@ -341,6 +364,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
   const int rows_valid = min(32, R - (g * kRowsWG + 32 * wave));
 
   const float scale2 = p.sm_scale * kLog2e;
+  const float pthr = __builtin_amdgcn_exp2f(p.fold_log2);  // probability bound of the reference checks (inf for huge fold_log2)
   const char* kvb = static_cast<const char*>(p.kv);
   const int64_t row_bytes = p.kv_stride * 2;
 
@@ -522,33 +546,8 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     };
     // The side work between MFMAs is issued in order with them: an
     // instruction that waits on the one before it (an exp on its fma, an add
-    // on its exp) holds back the next MFMA as well. So the block maximum is
-    // a tree of independent v_max3 (two per gap) and each probability is
+    // on its exp) holds back the next MFMA as well. So each probability is
     // three stages one gap apart.
-    //
-    // The block's maximum in six pieces: three gaps of two independent
-    // maxima of three scores, the maximum of those, then the lane-half swap.
-    float mx[6];
-    auto max_part = [&](int h, int part) {
-      if (part == 0) {
-        mx[0] = max3(sm[h][0], sm[h][1], sm[h][2]);
-        mx[1] = max3(sm[h][3], sm[h][4], sm[h][5]);
-      } else if (part == 1) {
-        mx[2] = max3(sm[h][6], sm[h][7], sm[h][8]);
-        mx[3] = max3(sm[h][9], sm[h][10], sm[h][11]);
-      } else if (part == 2) {
-        mx[4] = max3(sm[h][12], sm[h][13], sm[h][14]);
-        mx[5] = max3(mx[0], mx[1], sm[h][15]);
-      } else if (part == 3) {
-        tmx[h] = max3(mx[2], mx[3], mx[4]);
-      } else if (part == 4) {
-        tmx[h] = max3(tmx[h], mx[5], mx[5]);
-      } else {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx[h]), __float_as_uint(tmx[h]), false, false);
-        tmx[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
-      }
-    };
-    constexpr int kMaxParts = 6;
     // Probability j of block h against mu = -m_ref (0 while m_ref = -inf):
     // F (the fma into pt[j]), E (exp2 in place), S (the running sum, and for
     // odd j the pair packed into the P^T operand). prob_stage(h, k, mu) is
@@ -577,11 +576,20 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
 #pragma unroll
       for (int k = 0; k < kProbGaps; ++k) prob_stage(h, k, mu);
     };
+    // The block's maximum per row, scaled: a row's 32 keys sit in lanes col
+    // and col + 32. Only the reference checks below need it.
     auto max_block = [&](int h) {
+      float mx = sm[h][0];
 #pragma unroll
-      for (int part = 0; part < kMaxParts; ++part) max_part(h, part);
+      for (int j = 1; j < 15; j += 2) mx = max3(mx, sm[h][j], sm[h][j + 1]);
+      mx = fmaxf(mx, sm[h][15]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      tmx[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
     };
     const float mu0 = m_ref == -INFINITY ? 0.f : -m_ref;
+    // Keeps block h's probabilities and sum where they are computed (a
+    // reference check below recomputes them when the reference moves).
+    auto pin_probs = [&](int h) { asm volatile("" ::"v"(pf[2 * h]), "v"(pf[2 * h + 1]), "v"(psum[h])); };
 
     // ---- value product O^T += V^T P^T, step n: key step q = n / 16 (keys
     // 16q ..), entry block db = n % 16. Key step q = 2h + c takes score
@@ -633,7 +641,11 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
     // four MFMAs.
     // The rope part of the queries is read from LDS four k-steps before the
     // block's rope steps, right after that step's operand read, so the
-    // operand wait of the first rope step covers it as well.
+    // operand wait of the first rope step covers it as well. The last
+    // kVEarly steps read the first kVEarly value steps' operands, which so
+    // arrive under the last score MFMAs (the rest of the value ring is read
+    // after block 0's reference check: held across it, more of the ring
+    // would not fit the registers).
     const uint32_t qrbase = (uint32_t)(uintptr_t)TVMLA_LDS(const char, qrope) + (32 * wave + lcol) * kRopeRow;
     bf16x8_t ring[kSRing], qrf[kDRope / 16];
     static_for<0, kSRing>([&](auto x_) { ring[decltype(x_)::value] = sread(x_); });
@@ -646,11 +658,10 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         stage_chunk<j % kChunks>(nxt, sa, 2 * wave + j / kChunks);
       }
       bf16x8_t& kf = ring[n % kSRing];
-      // even steps wait for this step's and the next step's operands (at
-      // most the reads of the steps after n + 1 outstanding); the rope
-      // operands were read right after step 32's operand read, so step 32's
-      // wait covers them too
-      constexpr int ahead = kSSteps - 2 - n < kSRing - 2 ? kSSteps - 2 - n : kSRing - 2;
+      // even steps wait for this step's and the next step's operands: at
+      // most the LDS reads issued after step n + 1's operand read stay
+      // outstanding (LDS reads complete in order)
+      constexpr int ahead = s_reads_after(n + 1, n);
       static_assert(kQSteps % 2 == 0, "score steps wait in pairs within each block");
       const bf16x8_t& qop = ks < 32 ? qf[ks < 32 ? ks : 0] : qrf[ks < 32 ? 0 : ks - 32];
       if constexpr (ks == 0)
@@ -660,6 +671,7 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
       else
         TVMLA_MFMA_S_NW(sacc[kb], kf, qop);
       if constexpr (n + kSRing < kSSteps) kf = sread(Int<n + kSRing>{});
+      if constexpr (n >= kSSteps - kVEarly) vread(Int<n - (kSSteps - kVEarly)>{});
       static_assert(kSRing == 4, "the rope operand reads assume four operand reads in flight");
       if constexpr (ks == 32 - kSRing) {
         static_for<0, kDRope / 16>([&](auto c_) {
@@ -673,15 +685,14 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
         for (int j = 0; j < 16; ++j) sm[0][j] = sacc[0][j];
         mask_block(0);
       }
-      if constexpr (i >= 1 && i <= kMaxParts) max_part(0, i - 1);
-      constexpr int k0 = i - (kMaxParts + 1);  // gap of block 0's probability pipeline
+      constexpr int k0 = i - 1;        // gap of block 0's probability pipeline
       constexpr int g0 = k0 - k0 / 3;  // pipeline step of this gap (every third gap empty)
       if constexpr (k0 >= 0 && k0 % 3 != 2 && g0 < kProbGaps) prob_stage(0, g0, mu0);
-      static_assert(kQSteps + 2 + kMaxParts + (3 * kProbGaps) / 2 <= kSSteps, "block 0's softmax must fit under block 1's MFMAs");
-      // Keep them here: the reference decision below recomputes them when
-      // the reference moves, and the compiler would otherwise sink them into
-      // the other branch, after the last score MFMA.
-      if constexpr (k0 % 3 != 2 && g0 == kProbGaps - 1) asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(psum[0]));
+      static_assert(kQSteps + 2 + 1 + (3 * kProbGaps) / 2 <= kSSteps, "block 0's softmax must fit under block 1's MFMAs");
+      // Keep them here: the reference check below recomputes them when the
+      // reference moves, and the compiler would otherwise sink them into the
+      // other branch, after the last score MFMA.
+      if constexpr (k0 >= 0 && k0 % 3 != 2 && g0 == kProbGaps - 1) pin_probs(0);
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -714,33 +725,54 @@ void split_rows_kernel(SplitParams p, int groups, int pairs) {
 #pragma unroll
       for (int db = 0; db < 16; ++db) TVMLA_MFMA_ZERO(o[db], zero8);
     };
-    // Block 1's maximum, once its last MFMA's results are written.
-    asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc[1]));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sm[1][j] = sacc[1][j];
-    mask_block(1);
-    max_block(1);
-    const float tm = fmaxf(tmx[0], tmx[1]);
-    const bool grow = tm > m_ref + p.fold_log2;
-    if (__ballot(grow)) {
-      // A row's max outgrew its reference (always so on the first tile with
-      // a visible key): fold first if that row has accumulated something,
-      // move the reference, redo block 0's probabilities
-      if (__ballot(grow && m_ref != -INFINITY)) fold();
-      m_ref = grow ? tm : m_ref;
-      probs_block(0, m_ref == -INFINITY ? 0.f : -m_ref);
-    }
+    // Reference checks, one per key block. A block's probabilities are taken
+    // against the current reference; the reference has to move only when
+    // one of them exceeds 2^fold_log2 (the block's max outgrew the
+    // reference by more than fold_log2) or when a row with no reference yet
+    // (-inf) sees a key. A probability above the bound puts its lane's
+    // partial sum above it too (and an overflow makes the sum inf), so the
+    // lane sums decide: a wavefront with no such lane -- the common case --
+    // goes on with no maximum computed. Otherwise it computes the block's
+    // maximum and moves the reference as online softmax does: rows whose max
+    // outgrew the reference take it as their new one -- after the wavefront
+    // folds its accumulator into the rows' partial-result slots if they have
+    // accumulated something -- and the block's probabilities are redone.
+    // (Once set from data, a reference is some key's score, whose probability
+    // 1 keeps the row's sum from underflowing.)
+    auto vis_any = [&](int h) { return allvis || ((((uint32_t)(vh >> (32 * h))) & kVisAll) != 0u); };
+    auto check_block = [&](int h) {
+      const bool need = (m_ref == -INFINITY && vis_any(h)) || psum[h] >= pthr;
+      if (__ballot(need)) {
+        max_block(h);
+        const bool grow = tmx[h] > m_ref + p.fold_log2;
+        if (__ballot(grow && m_ref != -INFINITY)) fold();
+        m_ref = grow ? tmx[h] : m_ref;
+        probs_block(h, m_ref == -INFINITY ? 0.f : -m_ref);
+      }
+    };
+    check_block(0);
     const float mu1 = m_ref == -INFINITY ? 0.f : -m_ref;
+    static_for<kVEarly, kVRing>([&](auto x_) { vread(x_); });
 
-    // ---- value steps of block 0 while block 1's probabilities are
-    // computed alongside, then block 1's value steps
-    static_for<0, kVRing>([&](auto x_) { vread(x_); });
+    // ---- value steps of block 0 with block 1's probabilities computed
+    // alongside (against the reference block 0 left), block 1's check (a
+    // fold there takes block 0's products and sum with it), then block 1's
+    // value steps
     pv_steps(Int<0>{}, Int<32>{}, [&](auto i_) {
       constexpr int i = decltype(i_)::value;
+      if constexpr (i == 0) {
+        asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc[1]));  // block 1's last MFMA results are written
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sm[1][j] = sacc[1][j];
+        mask_block(1);
+      }
       constexpr int k1 = i - 1, g1 = k1 - k1 / 3;
       if constexpr (k1 >= 0 && k1 % 3 != 2 && g1 < kProbGaps) prob_stage(1, g1, mu1);
+      if constexpr (k1 >= 0 && k1 % 3 != 2 && g1 == kProbGaps - 1) pin_probs(1);
     });
-    l_part += psum[0] + psum[1];
+    l_part += psum[0];
+    check_block(1);
+    l_part += psum[1];
     pv_steps(Int<32>{}, Int<64>{}, [](auto) {});
     group_slots(slot_reg);  // for the tile after next, staged by the next tile
   };
