@@ -116,7 +116,8 @@ typedef enum {
  * keys would take a probability above 2^fold_log2 against it (the row's
  * scaled max, in log2 units, outgrew the reference by more than fold_log2).
  * A negative or infinite value selects the default, 16 (every probability
- * stays below 2^16); NaN is rejected with TVMLA_E_VALUE.
+ * stays below 2^16), and values above 64 are taken as 64 (larger ones would
+ * let probabilities overflow fp32); NaN is rejected with TVMLA_E_VALUE.
  * Results are the same for any threshold up to rounding: only the number of
  * folds changes (small thresholds make folds frequent, which tests use to
  * exercise that path). Other algorithms ignore it.

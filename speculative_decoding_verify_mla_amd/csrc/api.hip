@@ -39,9 +39,14 @@ tvmla_status check_shape(int32_t batch, int32_t num_draft, int32_t num_heads, in
 
 // Growth of a row's running max (log2 units) past which the row-owner
 // kernel folds its accumulator into the workspace: 16 (probabilities stay
-// below 2^16) unless the caller passes a threshold >= 0. Results are the same
-// for any threshold; only the number of folds changes.
-float fold_threshold(float fold_log2) { return fold_log2 >= 0.f && fold_log2 < INFINITY ? fold_log2 : 16.f; }
+// below 2^16) unless the caller passes a finite threshold >= 0. Thresholds
+// above 64 are taken as 64: a probability past 2^128 overflows fp32, and 64
+// leaves the sums and the value products room. Results are the same for any
+// threshold up to rounding; only the number of folds changes.
+float fold_threshold(float fold_log2) {
+  if (!(fold_log2 >= 0.f) || fold_log2 == INFINITY) return 16.f;
+  return fold_log2 < 64.f ? fold_log2 : 64.f;
+}
 
 // Splits the split+combine entry points run with TVMLA_FLAG_TUNE_NSPLIT: the caller's nsplit doubled
 // (up to TVMLA_MAX_NSPLIT) while the 128-row grid, batch * nsplit * ceil(T*H

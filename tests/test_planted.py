@@ -97,3 +97,18 @@ def test_planted_gpu(nsplit):
         log(f"[planted] nsplit {nsplit} algo {algo}: default fold threshold")
         out, lse = d.result(algo=algo, nsplit=nsplit)
         compare(w, out, lse, ref_out, ref_lse, f"planted/nsplit{nsplit}/algo{algo}")
+
+
+@pytest.mark.gpu
+def test_planted_gpu_large_threshold():
+    """fold_log2 above 64 is taken as 64: with a threshold of 1000 taken
+    literally the 180-unit plants would overflow fp32 probabilities."""
+    from speculative_decoding_verify_mla_amd import binding
+    from tests.gpu_util import Device, compare, log
+    w = planted_workload()
+    ref_out, ref_lse = _oracle(w)
+    d = Device(w, nsplit=1)
+    for fold in (64.0, 1000.0):
+        log(f"[planted] nsplit 1 row-owner kernel, fold threshold {fold}")
+        out, lse = d.result(algo=binding.ALGO_ROWS, nsplit=1, fold_log2=fold)
+        compare(w, out, lse, ref_out, ref_lse, f"planted/fold{fold}")
