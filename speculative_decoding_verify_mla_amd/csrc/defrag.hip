@@ -13,8 +13,12 @@
 // 0..7 load the 8 rows' slots, then the 8 x 72 16-byte chunks of the rows
 // (8 x 144 for fp32) are spread over the 64 lanes, 9 (18) per lane, all
 // loads issued before the first store. Each row is read and written as
-// contiguous 16-byte pieces; the chunk values stay in registers. HBM-bound:
-// per row 2 x 576 x elem_size bytes plus the 4-byte index.
+// contiguous 16-byte pieces; the chunk values stay in registers. Loads and
+// stores are non-temporal: the source rows are dead once copied and the
+// destination is read only by later verify calls, so the copy should not
+// displace what the L2s and the MALL hold (with ordinary loads, a copy that
+// finds the MALL full of other dirty lines pays for their write-back).
+// HBM-bound: per row 2 x 576 x elem_size bytes plus the 4-byte index.
 //
 // Index kernel: kv_indices_out[kv_indptr[b] + j] = dst_base[b] + j. It runs
 // after the copy on the same stream, so kv_indices_out may alias kv_indices.
@@ -27,6 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 8;  // rows per wavefront unit
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Nine chunks of a unit, chunk ids id = lane + 64 (K0 + k), k = 0..8: all
 // nine loads first, then the stores (named registers, so nothing goes to
@@ -40,9 +45,9 @@ __device__ __forceinline__ void copy_nine(const char* src, char* dst, const Defr
 #define TVMLA_LOAD(k)                                                         \
   TVMLA_CHUNK(k, r##k, c##k);                                                 \
   const int64_t s##k = __shfl(slot, r##k < nr ? r##k : nr - 1, 64);          \
-  const uint4 v##k = *reinterpret_cast<const uint4*>(src + s##k * d.src_row_bytes + 16 * c##k)
+  const u32x4 v##k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s##k * d.src_row_bytes + 16 * c##k))
 #define TVMLA_STORE(k) \
-  if (r##k < nr) *reinterpret_cast<uint4*>(dst + (drow0 + r##k) * d.dst_row_bytes + 16 * c##k) = v##k
+  if (r##k < nr) __builtin_nontemporal_store(v##k, reinterpret_cast<u32x4*>(dst + (drow0 + r##k) * d.dst_row_bytes + 16 * c##k))
   TVMLA_LOAD(0); TVMLA_LOAD(1); TVMLA_LOAD(2); TVMLA_LOAD(3); TVMLA_LOAD(4);
   TVMLA_LOAD(5); TVMLA_LOAD(6); TVMLA_LOAD(7); TVMLA_LOAD(8);
   TVMLA_STORE(0); TVMLA_STORE(1); TVMLA_STORE(2); TVMLA_STORE(3); TVMLA_STORE(4);
