@@ -46,12 +46,15 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* sink, int iters) 
 // cache rows of row_bytes (a multiple of 16, at most 2,304) from the slots
 // list, lanes 0..7 read the 8 slots, and the rows' 16-byte pieces are spread
 // over the 64 lanes with every load of a unit issued before any is used.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* src, size_t n16, unsigned* sink) {
-  uint4 acc = {0u, 0u, 0u, 0u};
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
-    const uint4 v = src[i];
-    acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
-  }
+// Both load non-temporally, as the verify kernels stage the cache rows: a
+// cold read that allocates in a MALL full of other dirty lines also pays
+// for their write-back.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* src, size_t n16, unsigned* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    acc ^= __builtin_nontemporal_load(src + i);
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[0] = 1u;
 }
 
@@ -62,22 +65,21 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* pool, long
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pieces = (int)(row_bytes / 16);
   const int per_lane = (8 * pieces + 63) / 64;  // at most 18
-  uint4 acc = {0u, 0u, 0u, 0u};
+  u32x4 acc = {0u, 0u, 0u, 0u};
   for (int u = blockIdx.x * 4 + wave; 8 * u < nrows; u += gridDim.x * 4) {
     const int nr = nrows - 8 * u < 8 ? nrows - 8 * u : 8;
     const long slot = lane < nr ? (long)slots[8 * u + lane] : 0;
-    uint4 v[(8 * kMaxPieces + 63) / 64];
+    u32x4 v[(8 * kMaxPieces + 63) / 64];
 #pragma unroll
     for (int k = 0; k < (8 * kMaxPieces + 63) / 64; ++k) {
-      v[k] = uint4{0u, 0u, 0u, 0u};
+      v[k] = u32x4{0u, 0u, 0u, 0u};
       const int id = lane + 64 * k, r = id / pieces, c = id - r * pieces;
       const long s = __shfl(slot, r < nr ? r : nr - 1, 64);
-      if (k < per_lane && r < nr) v[k] = *reinterpret_cast<const uint4*>(pool + s * row_bytes + 16 * c);
+      if (k < per_lane && r < nr)
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + s * row_bytes + 16 * c));
     }
 #pragma unroll
-    for (int k = 0; k < (8 * kMaxPieces + 63) / 64; ++k) {
-      acc.x ^= v[k].x; acc.y ^= v[k].y; acc.z ^= v[k].z; acc.w ^= v[k].w;
-    }
+    for (int k = 0; k < (8 * kMaxPieces + 63) / 64; ++k) acc ^= v[k];
   }
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[0] = 1u;
 }
@@ -91,7 +93,7 @@ extern "C" {
 int tvmla_probe_stream_read(const void* src, size_t bytes, unsigned* sink, int blocks, void* stream) {
   if (src == nullptr || sink == nullptr || blocks <= 0 || bytes % 16) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     static_cast<const uint4*>(src), bytes / 16, sink);
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
   return (int)hipGetLastError();
 }
 

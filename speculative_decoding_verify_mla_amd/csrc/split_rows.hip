@@ -286,11 +286,14 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 // offset, which the hardware adds to the global and to the LDS address
 // alike, so the LDS base given is 1024c - 128c past the group's (this spares
 // a 64-bit address add per load). The loads of a tile go one at a time over
-// the previous tile's score MFMAs.
+// the previous tile's score MFMAs. They are non-temporal (cache policy 2,
+// `nt`): a cold call whose loads allocate in a MALL full of other dirty
+// lines pays for their write-back (at 8 heads the cold split ran 104 us with
+// ordinary loads, 66 us with these, the warm split 63 us either way).
 template <int C>
 __device__ __forceinline__ void stage_chunk(char* dst, const char* a, int G) {
   __builtin_amdgcn_global_load_lds(a, TVMLA_LDS(void, dst + G * kGroupBytes + C * (kChunkBytes - kChunk)), 16,
-                                   kChunk * C, 0);
+                                   kChunk * C, 2);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
