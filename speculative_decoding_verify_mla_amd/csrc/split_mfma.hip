@@ -187,18 +187,22 @@ __device__ inline bf16x8_t cat4(i16x4_t lo, i16x4_t hi) {
 //           row, so a score read of one piece over 8 consecutive keys hits
 //           8 different bank groups. `row` is lane l's source row, the
 //           cache row of key k (fetched from lane k with a lane shuffle).
+// Both load non-temporally (cache policy 2, `nt`): a cold call whose loads
+// allocate in a MALL full of other dirty lines pays for their write-back (8
+// heads: cold call 158 -> 134 us at 64 splits; warm 126 -> 130 us, the two
+// row groups' shared key lines leaving the L2 sooner).
 __device__ __forceinline__ void stage_key(char* dst, uint32_t ra_lo, uint32_t ra_hi, int wave, int lane, int u) {
   const int k = 16 * wave + u;  // swz(k) depends on u only
   const uint64_t row_addr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ra_hi, k) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(ra_lo, k);
   const char* src = reinterpret_cast<const char*>(row_addr) + ((lane ^ piece_swz(k)) << 4);
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + k * kLatRow), 16, 0, 2);
 }
 
 __device__ __forceinline__ void stage_rope(char* dst, const char* row, int wave, int lane, int u) {
   const int v = 2 * wave + u;
   const char* src = row + kDLatent * 2 + 16 * ((lane & 7) ^ (lane >> 3));
-  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, TVMLA_LDS(void, dst + kTileLat + v * 8 * kRopeRow), 16, 0, 2);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
