@@ -339,13 +339,13 @@ tvmla_status tvmla_combine(const void* workspace, size_t workspace_bytes, const 
  * kv_indptr, kv_indices   as for tvmla_verify (read only).
  * dst_base         int32 [batch]: first destination slot of each request.
  * kv_indices_out   int32 [kv_indptr[batch]]: the rewritten indices; may be
- *                  kv_indices itself (the index rewrite is enqueued after
- *                  the copy).
+ *                  kv_indices itself (each index is rewritten after it has
+ *                  been read, by the thread that read it).
  * Draft rows (out_cache_loc) are not moved. The destination runs must not
  * overlap each other or any source row of the same call (the caller picks
  * free slots); overlapping runs are undefined behaviour.
  * Alignment: caches 16-byte aligned, row strides multiples of 16 bytes.
- * Limits: 1 <= batch <= 65535. Enqueues two kernels on `stream`.
+ * Limits: 1 <= batch <= 65535. Enqueues one kernel on `stream`.
  */
 tvmla_status tvmla_defrag(const void* kv_src, int64_t src_stride_row, void* kv_dst, int64_t dst_stride_row,
                           const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* dst_base,

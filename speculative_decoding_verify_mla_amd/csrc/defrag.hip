@@ -20,8 +20,10 @@
 // finds the MALL full of other dirty lines pays for their write-back).
 // HBM-bound: per row 2 x 576 x elem_size bytes plus the 4-byte index.
 //
-// Index kernel: kv_indices_out[kv_indptr[b] + j] = dst_base[b] + j. It runs
-// after the copy on the same stream, so kv_indices_out may alias kv_indices.
+// The index rewrite, kv_indices_out[kv_indptr[b] + j] = dst_base[b] + j, is
+// done by the lane that reads kv_indices[kv_indptr[b] + j] for its unit,
+// after that read: no other thread reads the element, so kv_indices_out may
+// alias kv_indices, and no second launch is needed.
 
 #include "tvmla_internal.h"
 
@@ -73,17 +75,10 @@ __global__ __launch_bounds__(kThreads) void defrag_copy_kernel(DefragParams d) {
     const int j0 = u * kRows;
     const int nr = P - j0 < kRows ? P - j0 : kRows;  // rows of this unit (the request's last may be short)
     const int64_t slot = lane < nr ? (int64_t)d.kv_indices[i0 + j0 + lane] : 0;
+    if (lane < nr) d.indices_out[i0 + j0 + lane] = (int32_t)(dbase + j0 + lane);  // after this lane's read
     copy_nine<kChunks, 0>(src, dst, d, slot, nr, dbase + j0, lane);
     if constexpr (kRows * kChunks == 2 * 64 * 9) copy_nine<kChunks, 9>(src, dst, d, slot, nr, dbase + j0, lane);
   }
-}
-
-__global__ __launch_bounds__(kThreads) void defrag_index_kernel(DefragParams d) {
-  const int b = blockIdx.y;
-  const int i0 = d.kv_indptr[b];
-  const int P = d.kv_indptr[b + 1] - i0;
-  const int dbase = d.dst_base[b];
-  for (int j = blockIdx.x * kThreads + threadIdx.x; j < P; j += gridDim.x * kThreads) d.indices_out[i0 + j] = dbase + j;
 }
 
 }  // namespace
@@ -95,11 +90,7 @@ hipError_t launch_defrag(const DefragParams& d, int elem_size, hipStream_t strea
   void* args[] = {&arg};
   const void* fn = elem_size == 2 ? reinterpret_cast<const void*>(&defrag_copy_kernel<kDKey * 2 / 16>)
                                   : reinterpret_cast<const void*>(&defrag_copy_kernel<kDKey * 4 / 16>);
-  hipError_t e = hipLaunchKernel(fn, dim3(gx, (unsigned)d.batch), dim3(kThreads), args, 0, stream);
-  if (e != hipSuccess) return e;
-  const unsigned ix = (unsigned)std::max(1, std::min(256, (256 + d.batch - 1) / d.batch));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&defrag_index_kernel), dim3(ix, (unsigned)d.batch),
-                         dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(gx, (unsigned)d.batch), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace tvmla

@@ -37,7 +37,7 @@ def _kernels(text):
 def test_every_kernel_reported(report):
     names = " ".join(_kernels(report))
     for k in ("split_rows_kernel", "split_mfma_kernel", "split_scalar_kernel", "combine_kernel",
-              "defrag_copy_kernel", "defrag_index_kernel", "tree_mask_kernel"):
+              "defrag_copy_kernel", "tree_mask_kernel"):
         assert k in names, k
 
 
