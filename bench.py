@@ -215,19 +215,31 @@ def read_ceilings(torch, pool, kv_indices, kv_bytes):
             "bytes": stream_bytes, "rows": nrows, "row_bytes": int(row_bytes), "cache": "cold (1 GiB flushed)"}
 
 
+def code_digest(path):
+    """sha256 of a HIP source file's code: comments and blank space dropped,
+    so that editing a comment does not mark a profile of the file stale."""
+    import hashlib
+    import re
+
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(" ".join(line.split()) for line in text.split("\n") if line.strip())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def profiled_traffic(kernel):
     """HBM bytes per split launch of `kernel` (a csrc file stem) from the
     committed rocprofv3 summary, or None if there is none or the kernel's
-    source has changed since those counters were taken."""
-    import hashlib
+    code has changed since those counters were taken."""
     import re
 
     prof = os.path.join(ROOT, "profiles", f"{kernel}_long185k.md")
     src = os.path.join(ROOT, "speculative_decoding_verify_mla_amd", "csrc", f"{kernel}.hip")
     try:
         text = open(prof).read()
-        m = re.search(r"traffic_bytes_per_launch: fetch=(\d+) write=(\d+) source_sha256_prefix=([0-9a-f]+)", text)
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        m = re.search(r"traffic_bytes_per_launch: fetch=(\d+) write=(\d+) code_sha256_prefix=([0-9a-f]+)", text)
+        cur = code_digest(src)
     except OSError:
         return None
     if not m or not cur.startswith(m.group(3)):

@@ -3,19 +3,18 @@
  * Instinct MI355X (gfx950).
  *
  * One call computes the verify attention of a speculative-decoding draft tree:
- * every draft token of every request attends, with every head, to the
- * request's prefix keys and to the draft keys its visibility mask allows.
- * This is the call described on "The Architecture of Capture Safety:
- * Designing a CUDA Graph-Compatible Verify Kernel for SGLang", section "The
- * Design Emerges": a split-K flash-decode over a fixed number of splits
- * (first insight), prefix keys through kv_indices/kv_indptr and draft keys
- * through out_cache_loc with no concatenated copy (second insight), the raw
- * custom_mask/mask_indptr indexed in the kernel (third insight), prefix
- * lengths derived on the device from kv_indptr (fourth insight), and a
- * workspace the caller allocates once (fifth insight). The cache layout is
- * MLA's: one latent row per token, shared by every head, serving as the value
- * and as the first 512 entries of the key ("The Plan Document", section "The
- * Design Reasoning").
+ * every draft token of every request attends, with every head, to the request's
+ * prefix keys and to the draft keys its visibility mask allows. This is the
+ * call described on "The Architecture of Capture Safety: Designing a CUDA
+ * Graph-Compatible Verify Kernel for SGLang", section "The Design Emerges": a
+ * split-K flash-decode over a fixed number of splits (first insight), prefix
+ * keys through kv_indices/kv_indptr and draft keys through out_cache_loc with
+ * no concatenated copy (second insight), the raw custom_mask/mask_indptr
+ * indexed in the kernel (third insight), prefix lengths derived on the device
+ * from kv_indptr (fourth insight), and a workspace the caller allocates once
+ * (fifth insight). The cache layout is MLA's: one latent row per token, shared
+ * by every head, serving as the value and as the first 512 entries of the key
+ * ("The Plan Document", section "The Design Reasoning").
  *
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers unless stated otherwise; the
@@ -124,10 +123,10 @@ typedef enum {
  */
 
 /*
- * Bytes of workspace a verify call needs: the per-split partial results
- * (page 1, "Assumptions and Their Validity", assumption 3: a fixed
- * workspace sized from batch and constants only). It depends only on its
- * arguments, never on sequence lengths. Returns 0 for out-of-range
+ * Bytes of workspace a verify call needs: the per-split partial results ("The
+ * Architecture of Capture Safety", "Assumptions and Their Validity", assumption
+ * 3: a fixed workspace sized from batch and constants only). It depends only on
+ * its arguments, never on sequence lengths. Returns 0 for out-of-range
  * arguments.
  *
  * The size covers both nsplit splits (the count tvmla_verify runs, and
@@ -172,8 +171,8 @@ size_t tvmla_workspace_bytes(int32_t batch, int32_t num_draft, int32_t num_heads
  *               and positive (a softmax temperature), else TVMLA_E_VALUE
  * nsplit        splits per request, used exactly as given: split s covers
  *               keys [s*chunk, min((s+1)*chunk, N_b)), chunk =
- *               ceil(N_b/nsplit) (page 1, "The NSPLIT Calculation"); empty
- *               splits return at once. (tvmla_verify_ex with
+ *               ceil(N_b/nsplit) ("The Architecture of Capture Safety",
+ *               "The NSPLIT Calculation"); empty splits return at once. (tvmla_verify_ex with
  *               TVMLA_FLAG_TUNE_NSPLIT adapts the count to the GPU.)
  * out      [batch*num_draft, num_heads, 512] dtype, contiguous; bf16 output
  *          is rounded to nearest even
@@ -303,9 +302,9 @@ tvmla_status tvmla_verify_partials(const void* q_nope, int64_t q_nope_stride_tok
 
 /*
  * The combine step alone: merge per-split partials laid out as in
- * tvmla_workspace_bytes (the reduce of page 1, "The Design Emerges", first
- * insight). out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse),
- * lse = max lse + log(sum_s w_s).
+ * tvmla_workspace_bytes (the reduce of "The Architecture of Capture Safety",
+ * "The Design Emerges", first insight). out = sum_s w_s o_s / sum_s w_s with
+ * w_s = exp(lse_s - max lse), lse = max lse + log(sum_s w_s).
  *
  * If kv_indptr is non-NULL, split s of request b is read only when it holds
  * keys under the schedule above (N_b = kv_indptr[b+1]-kv_indptr[b]+num_draft,

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE. Only tests/ may call this; it exists to pin the
 vectorised fp64 oracle in verify_fp64.py with an independently written
 pure-Python version: explicit loops over (request, draft token, head, key),
 dot products and sums accumulated with math.fsum (exactly rounded), and the
-same definition (page 1, "The Design Emerges": prefix keys through
+same definition ("The Architecture of Capture Safety", "The Design Emerges": prefix keys through
 kv_indices/kv_indptr, draft keys through out_cache_loc, mask through
-custom_mask/mask_indptr; page 2, "The Design Reasoning": the 512-wide latent
+custom_mask/mask_indptr; "The Plan Document", "The Design Reasoning": the 512-wide latent
 is both the value and the first 512 key entries, shared by all heads).
 It shares no code with verify_fp64.py.
 """

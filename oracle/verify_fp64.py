@@ -9,27 +9,30 @@ fp64, per (request, draft token, head):
 
   keys of request b      prefix tokens through kv_indices[kv_indptr[b] :
                          kv_indptr[b+1]], then the request's draft tokens
-                         through out_cache_loc (page 1, "The Design Emerges",
-                         second and fourth insights);
+                         through out_cache_loc ("The Architecture of Capture
+                         Safety", "The Design Emerges", second and fourth
+                         insights);
   key vector             the full 576-wide cache row (512-wide latent, shared
                          by every head, then the 64-wide rope part); value
-                         vector = the 512-wide latent (page 2, "The Design
-                         Reasoning": one latent vector per token serves all
-                         heads);
+                         vector = the 512-wide latent ("The Plan Document",
+                         "The Design Reasoning": one latent vector per token
+                         serves all heads);
   visibility             custom_mask bytes at mask_indptr[b], one row of
-                         (prefix + draft) columns per draft token (page 1,
-                         "The Design Emerges", third insight; which draft
-                         token sees which key: page 1, "Input Knowledge
-                         Required", DDTree paragraph);
+                         (prefix + draft) columns per draft token ("The
+                         Architecture of Capture Safety", "The Design
+                         Emerges", third insight; which draft token sees
+                         which key: same page, "Input Knowledge Required",
+                         DDTree paragraph);
   score                  sm_scale * (q_nope . latent + q_rope . rope);
   result                 out = softmax-weighted mean of the visible values,
                          lse = natural log of the sum of exp(score) over the
                          visible keys.
 
-The split-K form (partials per key range, then a log-sum-exp merge; page 1,
-"The Design Emerges", first insight, and "The NSPLIT Calculation") reaches
-the same result exactly up to rounding; `split_range`, `verify_partials` and
-`combine` write that schedule out so tests can check the identity.
+The split-K form (partials per key range, then a log-sum-exp merge; "The
+Architecture of Capture Safety", "The Design Emerges", first insight, and
+"The NSPLIT Calculation") reaches the same result exactly up to rounding;
+`split_range`, `verify_partials` and `combine` write that schedule out so
+tests can check the identity.
 
 Readings of points the pages leave open:
   * kv_indptr spans the prefix only; the T draft tokens follow it, so a
@@ -69,7 +72,7 @@ def _i64(x) -> np.ndarray:
 
 def key_slots(kv_indptr, kv_indices, out_cache_loc, b: int, num_draft: int) -> np.ndarray:
     """Pool slot of each of request b's N_b keys: prefix via kv_indices, then
-    drafts via out_cache_loc (page 1, "The Design Emerges", second insight)."""
+    drafts via out_cache_loc ("The Architecture of Capture Safety", "The Design Emerges", second insight)."""
     ip = _i64(kv_indptr)
     prefix = _i64(kv_indices)[ip[b]:ip[b + 1]]
     drafts = _i64(out_cache_loc)[b * num_draft:(b + 1) * num_draft]
@@ -78,7 +81,7 @@ def key_slots(kv_indptr, kv_indices, out_cache_loc, b: int, num_draft: int) -> n
 
 def visibility(custom_mask, mask_indptr, b: int, num_draft: int, n_keys: int) -> np.ndarray:
     """Bool [T, N_b]: row i = draft token i, column p = key p of request b
-    (page 1, "The Design Emerges", third insight)."""
+    ("The Architecture of Capture Safety", "The Design Emerges", third insight)."""
     mi = _i64(mask_indptr)
     flat = _i64(custom_mask) if not hasattr(custom_mask, "detach") else custom_mask.detach().cpu().numpy()
     start = int(mi[b])
@@ -146,7 +149,7 @@ def verify_ragged(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc
                   mask_indptr, qo_indptr, sm_scale: float):
     """Oracle for draft trees of different sizes: request b owns query tokens
     qo_indptr[b] .. qo_indptr[b+1]-1 (T_b of them; the int64 token offsets of
-    page 1, "Input Knowledge Required"), its draft keys are out_cache_loc at
+    "The Architecture of Capture Safety", "Input Knowledge Required"), its draft keys are out_cache_loc at
     the same positions, its mask block is [T_b][P_b + T_b] at mask_indptr[b].
     Returns out [qo_indptr[-1], H, 512] and lse [qo_indptr[-1], H], fp64."""
     qn_all = _f64(q_nope)
@@ -204,7 +207,7 @@ def verify_rows(q_nope, q_rope, kv_cache, kv_indptr, kv_indices, out_cache_loc, 
 
 def split_range(n_keys: int, nsplit: int, s: int):
     """Key range [start, end) of split s: chunk = ceil(N / nsplit), split s
-    starts at s*chunk; it is empty when start >= end (page 1, "The Design
+    starts at s*chunk; it is empty when start >= end ("The Architecture of Capture Safety", "The Design
     Emerges", first insight, and "The NSPLIT Calculation")."""
     chunk = -(-n_keys // nsplit) if n_keys > 0 else 0
     start = s * chunk
@@ -252,7 +255,7 @@ def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
     o_parts, axis -1 of lse_parts): weights exp(lse_s - max lse), out = weighted
     mean of the normalised partials, lse = max + log(sum of weights). Splits
     with lse_s = -inf weigh nothing; if every split is -inf the row is empty
-    (out = 0, lse = -inf). This is the reduce step of page 1, "The Design
+    (out = 0, lse = -inf). This is the reduce step of "The Architecture of Capture Safety", "The Design
     Emerges", first insight."""
     lse_parts = np.asarray(lse_parts, dtype=np.float64)
     o_parts = np.asarray(o_parts, dtype=np.float64)

@@ -1,12 +1,12 @@
 // C ABI of tvmla: host-side argument checks, workspace carving, launches.
 //
 // Every check runs before the first HIP call, so a rejected call enqueues
-// nothing and touches no device state. A call that passes enqueues exactly
-// two kernels on the caller's stream (split, then combine); the launch
-// configuration depends only on (batch, num_draft, num_heads, nsplit), so
-// the pair can be captured into a hipGraph once and replayed while the
-// metadata buffers change underneath (page 1, "The Core Problem": graph
-// replay reissues the same launches at the same addresses).
+// nothing and touches no device state. A call that passes enqueues exactly two
+// kernels on the caller's stream (split, then combine); the launch
+// configuration depends only on (batch, num_draft, num_heads, nsplit), so the
+// pair can be captured into a hipGraph once and replayed while the metadata
+// buffers change underneath ("The Architecture of Capture Safety", "The Core
+// Problem": graph replay reissues the same launches at the same addresses).
 
 #include "../../include/tvmla.h"
 #include "tvmla_internal.h"

@@ -1,8 +1,9 @@
 // Combine kernel: log-sum-exp merge of the per-split partial results.
 //
-// The reduce step of the split-K flash-decode (page 1, "The Design Emerges",
-// first insight). Split s left o_s (its output, normalised by its own
-// softmax sum) and lse_s (natural log of that sum); the merged row is
+// The reduce step of the split-K flash-decode ("The Architecture of Capture
+// Safety", "The Design Emerges", first insight). Split s left o_s (its output,
+// normalised by its own softmax sum) and lse_s (natural log of that sum); the
+// merged row is
 //   M = max_s lse_s,  w_s = exp(lse_s - M),
 //   out = sum_s w_s o_s / sum_s w_s,  lse = M + log(sum_s w_s).
 // Splits that hold no keys under the schedule never wrote anything and are

@@ -1,12 +1,11 @@
 // bf16 MFMA split kernel for gfx950.
 //
-// Work unit: one workgroup = (request b, split s, group of 64 query rows).
-// A request's rows are r = i*H + h (draft token i, head h). Every row of a
-// request attends to the same keys, so one key tile staged in LDS feeds all
-// 64 rows of the group -- the "read the shared latent once, use it for many
-// heads" reuse of "The Plan Document", section "The Design Reasoning"
-// (variants 2 and 3), taken further because the products run on the matrix
-// cores.
+// Work unit: one workgroup = (request b, split s, group of 64 query rows). A
+// request's rows are r = i*H + h (draft token i, head h). Every row of a
+// request attends to the same keys, so one key tile staged in LDS feeds all 64
+// rows of the group -- the "read the shared latent once, use it for many heads"
+// reuse of "The Plan Document", section "The Design Reasoning" (variants 2 and
+// 3), taken further because the products run on the matrix cores.
 //
 // Tile = 64 keys, staged whole with direct global->LDS loads (16 bytes per
 // lane, no registers involved), double-buffered: while the four wavefronts
@@ -31,16 +30,16 @@
 //   The output block O^T (128 latent entries x 64 rows, fp32) stays in
 //   registers across the split.
 //
-// Schedule and indexing follow page 1, "The Design Emerges": split s of a
-// request with N keys covers [s*chunk, min((s+1)*chunk, N)), chunk =
-// ceil(N / nsplit), an empty split returns at once (first insight); a key's
-// slot comes from kv_indices (prefix) or out_cache_loc (draft) (second);
-// the mask byte is custom_mask[mask_indptr[b] + i*N + p] (third); P_b comes
-// from kv_indptr (fourth). The online softmax (running max, running sum,
-// rescaled accumulator; page 1, "Input Knowledge Required") rescales the
-// accumulator only when a row's running max grows by more than 2^8 since the
-// last rescale, which keeps every probability below 256; the normalised
-// result is the same.
+// Schedule and indexing follow "The Architecture of Capture Safety", "The
+// Design Emerges": split s of a request with N keys covers [s*chunk,
+// min((s+1)*chunk, N)), chunk = ceil(N / nsplit), an empty split returns at
+// once (first insight); a key's slot comes from kv_indices (prefix) or
+// out_cache_loc (draft) (second); the mask byte is custom_mask[mask_indptr[b] +
+// i*N + p] (third); P_b comes from kv_indptr (fourth). The online softmax
+// (running max, running sum, rescaled accumulator; "The Architecture of Capture
+// Safety", "Input Knowledge Required") rescales the accumulator only when a
+// row's running max grows by more than 2^8 since the last rescale, which keeps
+// every probability below 256; the normalised result is the same.
 
 #include "tvmla_internal.h"
 

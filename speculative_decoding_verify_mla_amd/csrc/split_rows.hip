@@ -2,12 +2,12 @@
 //
 // Work unit: one workgroup = (request b, split s, group of 128 query rows).
 // Wavefront w owns rows 32w .. 32w+31 of the group outright: it scores them
-// against all 64 keys of every tile, keeps their softmax state, and
-// accumulates their whole 512-entry output. Rows are r = i*H + h (draft token
-// i, head h); every row of a request attends to the same keys, so one key
-// tile staged in LDS feeds all 128 rows of the group ("The Plan Document",
-// section "The Design Reasoning", variants 2 and 3: read the shared latent
-// once, use it for many heads).
+// against all 64 keys of every tile, keeps their softmax state, and accumulates
+// their whole 512-entry output. Rows are r = i*H + h (draft token i, head h);
+// every row of a request attends to the same keys, so one key tile staged in
+// LDS feeds all 128 rows of the group ("The Plan Document", section "The Design
+// Reasoning", variants 2 and 3: read the shared latent once, use it for many
+// heads).
 //
 // LDS tile format: a 64-key tile is 8 groups of 8 keys. A key's cache row
 // is 9 chunks of 128 bytes (8 latent, 1 rope; one cache line each), and
@@ -22,11 +22,12 @@
 //            blocks, 36 k-steps each, v_mfma_f32_32x32x16_bf16; A = key rows
 //            read from LDS, B = the wavefront's 32 queries, held in VGPRs for
 //            the whole split);
-//   softmax  each lane holds 32 of its row's 64 scores, so the row maximum is
-//            a register maximum and one swap of lane halves -- no LDS
-//            exchange and no barrier. The probabilities, rounded to bf16,
-//            already sit in the lanes and order the value product takes as
-//            its B operand;
+//   softmax  each lane holds 32 of its row's 64 scores, so a row maximum --
+//            taken only when a key block's probabilities outgrow the
+//            reference (below) -- is a register maximum and one swap of lane
+//            halves: no LDS exchange and no barrier. The probabilities,
+//            rounded to bf16, already sit in the lanes and order the value
+//            product takes as its B operand;
 //   values   O^T += V^T P^T over all 512 latent entries (16 entry blocks x 4
 //            key steps of 16), V^T read with the transposed LDS read
 //            (ds_read_b64_tr_b16). O^T (512 x 32 fp32) lives in the 256
@@ -38,22 +39,22 @@
 // the queries come in, and the output rows go out, through them, so that
 // those memory accesses are whole rows rather than pieces of 32 rows.
 //
-// Split bounds, key slots, mask bytes and P_b follow page 1, "The Design
-// Emerges" (chunk = ceil(N / nsplit), rounded up to whole 64-key tiles when
-// the caller asks for that; empty split returns at once; slot from
-// kv_indices for the prefix and out_cache_loc for draft keys; mask byte
-// custom_mask[mask_indptr[b] + i*N + p]; P_b from kv_indptr). The online
-// softmax (page 1, "Input Knowledge Required": running max, running sum,
-// rescaled accumulator) keeps a per-row reference max and leaves the
-// accumulator alone while the row's max stays within 2^fold_log2 of it
-// (fold_log2 = 16: every probability stays below 65,536). When a row
-// outgrows that, the wavefront folds: the accumulator goes to the rows'
-// partial-result slots in the workspace (adding in what earlier folds left
-// there, brought to the current reference), restarts from zero, and the
-// reference moves up. The accumulator is never touched by vector
-// instructions inside the tile loop -- only by MFMAs and by stores that read
-// it straight from the AGPRs -- which is what keeps the compiler from moving
-// it to VGPRs. The normalised result is the same for any threshold.
+// Split bounds, key slots, mask bytes and P_b follow "The Architecture of
+// Capture Safety", "The Design Emerges" (chunk = ceil(N / nsplit), rounded up
+// to whole 64-key tiles when the caller asks for that; empty split returns at
+// once; slot from kv_indices for the prefix and out_cache_loc for draft keys;
+// mask byte custom_mask[mask_indptr[b] + i*N + p]; P_b from kv_indptr). The
+// online softmax ("The Architecture of Capture Safety", "Input Knowledge
+// Required": running max, running sum, rescaled accumulator) keeps a per-row
+// reference max and leaves the accumulator alone while the row's max stays
+// within 2^fold_log2 of it (fold_log2 = 16: every probability stays below
+// 65,536). When a row outgrows that, the wavefront folds: the accumulator goes
+// to the rows' partial-result slots in the workspace (adding in what earlier
+// folds left there, brought to the current reference), restarts from zero, and
+// the reference moves up. The accumulator is never touched by vector
+// instructions inside the tile loop -- only by MFMAs and by stores that read it
+// straight from the AGPRs -- which is what keeps the compiler from moving it to
+// VGPRs. The normalised result is the same for any threshold.
 
 #include "tvmla_internal.h"
 

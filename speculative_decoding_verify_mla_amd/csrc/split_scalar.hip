@@ -1,14 +1,15 @@
 // Scalar split kernel: one 64-lane wavefront per (query row, split), fp32 FMA.
 //
-// It serves the fp32 dtype and is the plain, easy-to-audit path for bf16.
-// Each wavefront walks its split's key range one key at a time (page 1,
-// "The Design Emerges", first insight: split s covers
+// It serves the fp32 dtype and is the plain, easy-to-audit path for bf16. Each
+// wavefront walks its split's key range one key at a time ("The Architecture of
+// Capture Safety", "The Design Emerges", first insight: split s covers
 // [s*chunk, min((s+1)*chunk, N)) with chunk = ceil(N / nsplit), and an empty
 // split returns at once), resolves the key's cache slot from kv_indices
 // (prefix) or out_cache_loc (draft tokens) (second insight), reads the
-// visibility byte from custom_mask at mask_indptr[b] + i*N + p (third
-// insight), and keeps an online softmax: running max m, running sum l and a
-// rescaled output accumulator o (page 1, "Input Knowledge Required").
+// visibility byte from custom_mask at mask_indptr[b] + i*N + p (third insight),
+// and keeps an online softmax: running max m, running sum l and a rescaled
+// output accumulator o ("The Architecture of Capture Safety", "Input Knowledge
+// Required").
 //
 // Lane l owns latent entries [8l, 8l+8) and rope entry l of the 576-wide
 // key, so one cache row is read as 64 contiguous 16-byte pieces plus one

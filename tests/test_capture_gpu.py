@@ -2,7 +2,7 @@
 tvmla_verify, and tvmla_verify_ragged, each captured once and replayed with
 new prefix lengths, trees and token counts written into the same buffers.
 Every replay matches the oracle and the eager call (capture safety: the
-launches depend only on scalars; page 1, "The Design Emerges")."""
+launches depend only on scalars; "The Architecture of Capture Safety", "The Design Emerges")."""
 import numpy as np
 import pytest
 import torch

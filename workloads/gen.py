@@ -3,13 +3,13 @@
 Every input the verify call consumes is drawn here: query vectors, latent
 cache rows, draft-tree shapes, page_size=1 slot choices, and the metadata
 arrays (kv_indptr / kv_indices / out_cache_loc / custom_mask / mask_indptr)
-in the layout the serving engine hands to its attention backend (page 1,
+in the layout the serving engine hands to its attention backend ("The Architecture of Capture Safety",
 "The Design Emerges": the prefix is addressed through kv_indices and
 kv_indptr, the draft tokens through out_cache_loc, and the visibility mask
 through custom_mask plus mask_indptr).
 
 Nothing here computes attention. Tree visibility ("a draft token sees the
-whole prefix, its ancestors and itself", page 1, "Input Knowledge Required")
+whole prefix, its ancestors and itself", "The Architecture of Capture Safety", "Input Knowledge Required")
 is input construction: it turns a parent array into mask bytes.
 
 Draw order per workload (one numpy PCG64 stream, fixed seed):
