@@ -12,8 +12,15 @@ tvmla_verify_partials on the same stream), and the fp64 CPU oracle timed on
 the same workload (whole, or a bounded sample). The line also carries the
 pages' own call -- tvmla_verify at exactly the workload's NSPLIT -- timed
 the same way, the call captured in a HIP graph and replayed warm and cold
-(L2 and MALL flushed before each replay), and the HBM copy bandwidth and
-bf16 MFMA rate measured on the same GPU.
+(L2 and MALL flushed before each replay), the HBM copy bandwidth and bf16
+MFMA rate measured on the same GPU, and what the part sustains cold for the
+call's bytes (a streaming read and a gather of the cache rows, with the
+non-temporal loads the kernels use).
+
+    python bench.py --op defrag|tree_mask [--workload W]
+
+times the compaction kernel (cold copy rate as the value, warm beside it)
+or the device-side tree mask instead.
 
     python bench.py --report
 
